@@ -1,0 +1,281 @@
+"""Plain CPU oracle for Hidden Decoding's Stream-Factorized Attention (SFA).
+
+TEST INFRASTRUCTURE ONLY.  This module is the slow, obviously-correct reference
+that the HIP path is checked against.  Only ``tests/``, ``__graft_entry__.smoke``
+and the CPU-baseline leg of ``bench.py`` may import it; the library itself never
+does, and it shares no code with the HIP sources.
+
+Everything here is float64 NumPy computed from the exact bf16 input bits.  Each
+function names the passage it follows:
+
+* "Hidden Decoding at Scale" review (romaanj.github.io), section *Method*: each
+  token becomes n streams through n independent embedding tables and the
+  backbone runs once over the length-nL sequence; most layers attend only inside
+  their own stream (cost of order nL^2), a few layers mix streams with the base
+  model's own (full causal) pattern; the intermediate streams' KV is retained
+  so later tokens read it as context.
+* arXiv 2607.08186 abstract page: SFA makes the attention cost grow roughly
+  linearly in n instead of quadratically.
+* Tencent/Sequential-Hidden-Decoding README, *Key Idea* items 1, 2 and 4.
+
+Readings where the pages are silent (each listed in the design notes):
+  R1 expanded position of (token t, stream s) is p = t*n + s (token-major
+     interleave, stream 0 first);
+  R2 table s feeds stream s;
+  R3 a within-stream query sees its own position (t' <= t);
+  R4 a mixing query at (t, s) sees (t, s') for s' <= s (causal in the
+     interleaved order);
+  R5 the softmax scale is an explicit argument;
+  R6 query head h reads KV head h // (Hq / Hkv);
+  R7 an out-of-range token id yields an all-zero row and raises a flag.
+
+No function here is "parity unpinned": every one is pinned in
+``tests/test_oracle.py`` against brute force, a library routine, a closed form
+or an invariant.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+WITHIN = 0  # within-stream layer
+MIX = 1     # mixing layer, full causal over the interleaved order
+
+
+# ---------------------------------------------------------------------------
+# bf16 handling
+# ---------------------------------------------------------------------------
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16/int16) to float64 exactly.
+
+    A bf16 value is the upper half of an IEEE float32, so shifting the 16 bits
+    into the high half of a 32-bit word gives the float32 with the same value;
+    widening float32 -> float64 is exact.
+    """
+    b = np.asarray(bits)
+    u32 = b.astype(np.uint16).astype(np.uint32) << np.uint32(16)
+    return u32.view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# (1) Embedding expansion + interleave
+# ---------------------------------------------------------------------------
+def expanded_position(t, s, n):
+    """Position of token t, stream s in the length-nL sequence (reading R1)."""
+    return t * n + s
+
+
+def expand_ref(ids, tables):
+    """Hidden Decoding embedding expansion (review, *Method*; README *Key Idea* 1-2).
+
+    ids    : int array [B, L] of token ids
+    tables : uint16 bf16 bits [n, V, H], table s is stream s's own embedding
+             table (reading R2)
+    returns (out, bad): out uint16 [B, n*L, H] with
+             out[b, t*n + s, :] = tables[s, ids[b, t], :]
+             and ``bad`` True when some id lies outside [0, V); such a token's
+             n rows are zero (reading R7).
+
+    Pure byte copy: no floating-point arithmetic is involved.
+    """
+    ids = np.asarray(ids)
+    tables = np.asarray(tables, dtype=np.uint16)
+    B, L = ids.shape
+    n, V, H = tables.shape
+    out = np.zeros((B, n * L, H), dtype=np.uint16)
+    bad = False
+    for b in range(B):
+        for t in range(L):
+            tok = int(ids[b, t])
+            if tok < 0 or tok >= V:
+                bad = True
+                continue
+            for s in range(n):
+                out[b, expanded_position(t, s, n), :] = tables[s, tok, :]
+    return out, bad
+
+
+def final_stream_rows_ref(x, n):
+    """Rows of the final stream, the only positions whose next-token loss is
+    taken (review, *Method*; README *Key Idea* 3): x[:, t*n + n-1, ...]."""
+    x = np.asarray(x)
+    L = x.shape[1] // n
+    idx = [expanded_position(t, n - 1, n) for t in range(L)]
+    return x[:, idx]
+
+
+def cyclic_replicate_ref(tables, n_new):
+    """Cyclic Replication Initialization (review, *Method*): when the number of
+    streams grows, the new tables are copies of the existing ones, cycling over
+    them: new table s = old table (s mod n_old)."""
+    tables = np.asarray(tables)
+    n_old = tables.shape[0]
+    return np.stack([tables[s % n_old] for s in range(n_new)], axis=0)
+
+
+# ---------------------------------------------------------------------------
+# (2) The SFA visibility rule
+# ---------------------------------------------------------------------------
+def visible(i, j, n, mode):
+    """True where key position j is visible to query position i.
+
+    Within-stream (review, *Method*: "attend only within their own stream"):
+        j and i hold the same stream (j = i mod n) and j is not later than i
+        (reading R3, so a query sees itself).
+    Mixing, full pattern (review, *Method*: the base model's own full causal
+        pattern, here over the interleaved order, reading R4): j <= i.
+
+    Works elementwise on NumPy integer arrays (broadcasting).
+    """
+    i = np.asarray(i)
+    j = np.asarray(j)
+    causal = j <= i
+    if mode == WITHIN:
+        return causal & ((j % n) == (i % n))
+    if mode == MIX:
+        return causal
+    raise ValueError(f"unknown mode {mode}")
+
+
+def count_pairs(N, n, mode):
+    """Number of visible (query, key) pairs in one (batch, head) of length N,
+    counted by enumerating the visibility rule (used to check the closed forms
+    n*L*(L+1)/2 and N*(N+1)/2 and the review's O(nL^2) vs O(n^2 L^2) orders)."""
+    j = np.arange(N)[None, :]
+    total = 0
+    for r0 in range(0, N, 1024):
+        i = np.arange(r0, min(N, r0 + 1024))[:, None]
+        total += int(np.count_nonzero(visible(i, j, n, mode)))
+    return total
+
+
+# ---------------------------------------------------------------------------
+# (3) Masked softmax attention, the plain definition
+# ---------------------------------------------------------------------------
+def _softmax_rows(scores):
+    """Row softmax of a float64 matrix whose masked entries are -inf.  Every row
+    holds at least one finite entry (the query's own position)."""
+    m = scores.max(axis=1, keepdims=True)
+    p = np.exp(scores - m)
+    return p / p.sum(axis=1, keepdims=True)
+
+
+def attention_rows(q_rows, q_pos, k, v, n, mode, scale):
+    """softmax(scale * q k^T + mask) v for some query rows of one head.
+
+    q_rows : float64 [R, D]   the queries
+    q_pos  : int [R]          their positions in the expanded sequence
+    k, v   : float64 [Nk, D]  keys/values at positions 0..Nk-1
+    returns (out [R, D], probs [R, Nk]) in float64.
+    """
+    j = np.arange(k.shape[0])[None, :]
+    mask = visible(np.asarray(q_pos)[:, None], j, n, mode)
+    scores = scale * (q_rows @ k.T)
+    scores = np.where(mask, scores, -np.inf)
+    probs = _softmax_rows(scores)
+    return probs @ v, probs
+
+
+def prefill_ref(q, k, v, n, mode, scale, rows=None, heads=None, batches=None,
+                chunk=1024):
+    """Prefill SFA layer (review, *Method*; abstract; README *Key Idea*).
+
+    q      : bf16 bits [B, N, Hq, D]; k, v : bf16 bits [B, N, Hkv, D];
+             N = n*L in the interleaved order (reading R1)
+    mode   : WITHIN or MIX
+    rows   : optional int array of query positions to compute (default all)
+    heads  : optional query heads (default all); batches likewise
+    returns float64 [len(batches), len(rows), len(heads), D]
+
+    Query head h reads KV head h // (Hq // Hkv) (reading R6).  Rows are handled
+    ``chunk`` at a time only to bound memory; each row's arithmetic is the
+    definition above, independent of the others.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    heads = list(range(Hq)) if heads is None else list(heads)
+    batches = list(range(B)) if batches is None else list(batches)
+    out = np.zeros((len(batches), len(rows), len(heads), D))
+    for bi, b in enumerate(batches):
+        for hi, h in enumerate(heads):
+            g = h // G
+            kf = bf16_bits_to_f64(k[b, :, g, :])
+            vf = bf16_bits_to_f64(v[b, :, g, :])
+            for c0 in range(0, len(rows), chunk):
+                r = rows[c0:c0 + chunk]
+                # keys later than the last requested row are never visible
+                nk = int(r.max()) + 1
+                qf = bf16_bits_to_f64(q[b, r, h, :])
+                o, _ = attention_rows(qf, r, kf[:nk], vf[:nk], n, mode, scale)
+                out[bi, c0:c0 + len(r), hi, :] = o
+    return out
+
+
+# ---------------------------------------------------------------------------
+# (4) Decode step over the retained KV cache
+# ---------------------------------------------------------------------------
+def decode_append_ref(k_cache, v_cache, k_new, v_new, tokens_before, n):
+    """Retained-KV append (review, *Method* and *Limitations*: every stream's
+    KV stays in the cache).  For sequence q with T = tokens_before[q] tokens
+    already cached, new stream s goes to entry T*n + s.  Returns new copies."""
+    kc = np.array(k_cache, dtype=np.uint16, copy=True)
+    vc = np.array(v_cache, dtype=np.uint16, copy=True)
+    S = kc.shape[0]
+    for qi in range(S):
+        T = int(tokens_before[qi])
+        for s in range(n):
+            kc[qi, expanded_position(T, s, n)] = k_new[qi, s]
+            vc[qi, expanded_position(T, s, n)] = v_new[qi, s]
+    return kc, vc
+
+
+def decode_ref(q_new, k_cache, v_cache, tokens_before, n, mode, scale,
+               seqs=None):
+    """Decode attention for the n new stream positions of one token.
+
+    q_new  : bf16 bits [S, n, Hq, D], query of new stream s of sequence q sits
+             at position T*n + s with T = tokens_before[q]
+    k_cache, v_cache : bf16 bits [S, C, Hkv, D] already holding the appended
+             entries (see decode_append_ref); entries 0 .. T*n + n - 1 are live
+    returns float64 [len(seqs), n, Hq, D]
+
+    The visibility rule is the prefill one restricted to the new queries: the
+    within-stream query (T, s) reads entries t'*n + s, t' <= T; the mixing
+    query reads every entry up to and including T*n + s (review, *Method*;
+    small-batch decode being bandwidth-bound is the review's *Notes*).
+    """
+    q_new = np.asarray(q_new)
+    S, _, Hq, D = q_new.shape
+    Hkv = k_cache.shape[2]
+    G = Hq // Hkv
+    seqs = list(range(S)) if seqs is None else list(seqs)
+    out = np.zeros((len(seqs), n, Hq, D))
+    for si, qi in enumerate(seqs):
+        T = int(tokens_before[qi])
+        live = T * n + n
+        pos = np.array([expanded_position(T, s, n) for s in range(n)])
+        for h in range(Hq):
+            g = h // G
+            kf = bf16_bits_to_f64(k_cache[qi, :live, g, :])
+            vf = bf16_bits_to_f64(v_cache[qi, :live, g, :])
+            qf = bf16_bits_to_f64(q_new[qi, :, h, :])
+            o, _ = attention_rows(qf, pos, kf, vf, n, mode, scale)
+            out[si, :, h, :] = o
+    return out
+
+
+# ---------------------------------------------------------------------------
+# (5) Useful work (closed forms checked against count_pairs in the tests)
+# ---------------------------------------------------------------------------
+def useful_flops(B, n, L, Hq, D, mode):
+    """4*D FLOPs per visible (query, key) pair per query head: 2*D for the
+    score, 2*D for the value accumulation."""
+    N = n * L
+    pairs = count_pairs(N, n, mode)
+    return 4 * D * Hq * B * pairs

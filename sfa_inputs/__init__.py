@@ -1,0 +1,172 @@
+"""Seeded synthetic inputs for the SFA workloads.
+
+This module only draws random numbers and rounds them to bf16; it holds none
+of the method's arithmetic.  It is the one piece shared by the tests, the bench
+and the oracle checks: both the HIP path and the oracle consume the very same
+bits produced here.
+
+Workloads (all synthetic, seeded):
+  tiny    n=2, B=1, L=64, 2/2 heads, D=64, Q/K/V ~ N(0,1)/8, scale 1;
+          expansion vocab 1000, hidden 128, tables ~ N(0, 0.02)
+  n4      n=4, B=2, L=1024, 32/8 heads, D=128, Q ~ N(0,1)/sqrt(128),
+          K, V ~ N(0,1), scale 1; expansion vocab 151936, hidden 4096
+  n8stack n=8, B=1, L=2048, 32/8 heads, D=128, pre-scaled as n4; a stack of
+          three within-stream layers and one mixing layer
+  long    n=4, B=1, L=8192, 64/4 heads, D=128, pre-scaled as n4
+  decode  S=64 sequences, n=4, 4096 cached tokens (16384 entries) each,
+          32/8 heads, D=128, everything ~ N(0,1), scale 1/sqrt(128)
+
+Seeds: 0x5FA00000 + 100*workload_index + 10*layer + k, with k = 0 ids,
+1 tables, 2 Q, 3 K, 4 V, 5 K-cache, 6 V-cache, 7 new q/k/v.
+Values are drawn in float32 with ``torch.randn``, scaled, then rounded once to
+bf16 (round to nearest even).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+SEED_BASE = 0x5FA00000
+
+
+@dataclass(frozen=True)
+class PrefillCfg:
+    name: str
+    index: int
+    n: int
+    B: int
+    L: int
+    Hq: int
+    Hkv: int
+    D: int
+    q_std: float
+    kv_std: float
+    scale: float
+    vocab: int = 0
+    hidden: int = 0
+    table_std: float = 0.02
+    layers: tuple = ()          # layer kinds of a stack, e.g. ("within", "mix")
+
+    @property
+    def N(self) -> int:
+        return self.n * self.L
+
+
+@dataclass(frozen=True)
+class DecodeCfg:
+    name: str
+    index: int
+    S: int
+    n: int
+    T: int                       # tokens already cached per sequence
+    Hq: int
+    Hkv: int
+    D: int
+    scale: float
+    extra_capacity: int = 1      # tokens of head-room beyond T (>= 1 for the append)
+
+    @property
+    def C(self) -> int:          # cache capacity in entries
+        return (self.T + self.extra_capacity) * self.n
+
+
+TINY = PrefillCfg("tiny", 1, n=2, B=1, L=64, Hq=2, Hkv=2, D=64, q_std=1 / 8,
+                  kv_std=1 / 8, scale=1.0, vocab=1000, hidden=128,
+                  layers=("within", "mix"))
+N4 = PrefillCfg("n4", 2, n=4, B=2, L=1024, Hq=32, Hkv=8, D=128,
+                q_std=1 / math.sqrt(128), kv_std=1.0, scale=1.0, vocab=151936,
+                hidden=4096, layers=("within", "mix"))
+N8STACK = PrefillCfg("n8stack", 3, n=8, B=1, L=2048, Hq=32, Hkv=8, D=128,
+                     q_std=1 / math.sqrt(128), kv_std=1.0, scale=1.0,
+                     layers=("within", "within", "within", "mix"))
+LONG = PrefillCfg("long", 4, n=4, B=1, L=8192, Hq=64, Hkv=4, D=128,
+                  q_std=1 / math.sqrt(128), kv_std=1.0, scale=1.0,
+                  layers=("within", "mix"))
+DECODE = DecodeCfg("decode", 5, S=64, n=4, T=4096, Hq=32, Hkv=8, D=128,
+                   scale=1 / math.sqrt(128))
+
+PREFILL_CFGS = (TINY, N4, N8STACK, LONG)
+
+
+def seed_of(index: int, layer: int, k: int) -> int:
+    return SEED_BASE + 100 * index + 10 * layer + k
+
+
+def _gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def randn_bf16(shape, std: float, seed: int, device="cpu") -> torch.Tensor:
+    """float32 N(0,1) * std, rounded once to bf16 (RNE)."""
+    g = _gen(seed, device)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    return x.to(torch.bfloat16)
+
+
+def token_ids(B: int, L: int, vocab: int, seed: int, device="cpu") -> torch.Tensor:
+    """Uniform token ids in [0, vocab) as int32 [B, L]."""
+    g = _gen(seed, device)
+    return torch.randint(0, vocab, (B, L), generator=g, device=device,
+                         dtype=torch.int64).to(torch.int32)
+
+
+def tables(n: int, vocab: int, hidden: int, std: float, seed: int,
+           device="cpu") -> torch.Tensor:
+    """n stacked embedding tables [n, vocab, hidden] bf16, drawn table by table
+    (keeps the float32 peak to one table)."""
+    out = torch.empty((n, vocab, hidden), dtype=torch.bfloat16, device=device)
+    for s in range(n):
+        out[s] = randn_bf16((vocab, hidden), std, seed + 1000 * s, device)
+    return out
+
+
+def expand_inputs(cfg: PrefillCfg, device="cpu"):
+    ids = token_ids(cfg.B, cfg.L, cfg.vocab, seed_of(cfg.index, 0, 0), device)
+    tab = tables(cfg.n, cfg.vocab, cfg.hidden, cfg.table_std,
+                 seed_of(cfg.index, 0, 1), device)
+    return ids, tab
+
+
+def prefill_qkv(cfg: PrefillCfg, layer: int = 0, device="cpu", q_std=None,
+                kv_std=None, B=None, L=None):
+    """Q [B, nL, Hq, D], K and V [B, nL, Hkv, D] in bf16, interleaved order."""
+    B = cfg.B if B is None else B
+    L = cfg.L if L is None else L
+    q_std = cfg.q_std if q_std is None else q_std
+    kv_std = cfg.kv_std if kv_std is None else kv_std
+    N = cfg.n * L
+    q = randn_bf16((B, N, cfg.Hq, cfg.D), q_std, seed_of(cfg.index, layer, 2), device)
+    k = randn_bf16((B, N, cfg.Hkv, cfg.D), kv_std, seed_of(cfg.index, layer, 3), device)
+    v = randn_bf16((B, N, cfg.Hkv, cfg.D), kv_std, seed_of(cfg.index, layer, 4), device)
+    return q, k, v
+
+
+def decode_inputs(cfg: DecodeCfg, device="cpu", tokens_before=None, S=None, T=None):
+    """Cache [S, C, Hkv, D] (entries beyond the live ones hold random values
+    too: they must never be read), the new q/k/v, and tokens_before [S]."""
+    S = cfg.S if S is None else S
+    T = cfg.T if T is None else T
+    C = (T + cfg.extra_capacity) * cfg.n
+    kc = randn_bf16((S, C, cfg.Hkv, cfg.D), 1.0, seed_of(cfg.index, 0, 5), device)
+    vc = randn_bf16((S, C, cfg.Hkv, cfg.D), 1.0, seed_of(cfg.index, 0, 6), device)
+    seed = seed_of(cfg.index, 0, 7)
+    qn = randn_bf16((S, cfg.n, cfg.Hq, cfg.D), 1.0, seed, device)
+    kn = randn_bf16((S, cfg.n, cfg.Hkv, cfg.D), 1.0, seed + 1, device)
+    vn = randn_bf16((S, cfg.n, cfg.Hkv, cfg.D), 1.0, seed + 2, device)
+    if tokens_before is None:
+        tb = torch.full((S,), T, dtype=torch.int32, device=device)
+    else:
+        tb = torch.as_tensor(tokens_before, dtype=torch.int32, device=device)
+    return qn, kn, vn, kc, vc, tb
+
+
+def bits(t: torch.Tensor):
+    """bf16 torch tensor -> NumPy uint16 bit patterns (host copy)."""
+    import numpy as np
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)

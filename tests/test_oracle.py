@@ -1,0 +1,445 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each test ties the oracle to something other than itself: the pure-Python brute
+force (a different formulation of the visibility rule and of the softmax), a
+library routine (torch SDPA in float64, torch embedding), a closed form, an
+invariant, or a number the pages state.  The ``planted`` tests plant plausible
+mistakes in the oracle (on the CPU) and check that a pin catches each one.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import brute, sfa
+from oracle.sfa import MIX, WITHIN
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_bits(rng, shape, std=1.0):
+    x = torch.from_numpy(rng.standard_normal(shape).astype(np.float32) * std)
+    return x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _f(bits):
+    return sfa.bf16_bits_to_f64(bits)
+
+
+def _sdpa_causal(qf, kf, vf, scale):
+    """float64 torch SDPA, causal. qf [B, N, Hq, D], kf/vf [B, N, Hkv, D]."""
+    G = qf.shape[2] // kf.shape[2]
+    q = torch.from_numpy(qf).permute(0, 2, 1, 3)
+    k = torch.from_numpy(kf).permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    v = torch.from_numpy(vf).permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True,
+                                                         scale=scale)
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+# ---------------------------------------------------------------------------
+# bf16 widening
+# ---------------------------------------------------------------------------
+def test_bf16_known_values():
+    bits = np.array([0x3F80, 0xBF80, 0x4049, 0x0000, 0x8000, 0x0001, 0x7F80,
+                     0x3C00], dtype=np.uint16)
+    want = [1.0, -1.0, 3.140625, 0.0, -0.0, 2.0 ** -133, math.inf, 2.0 ** -7]
+    got = _f(bits)
+    assert list(got) == want
+
+
+def test_bf16_matches_torch_conversion():
+    rng = np.random.default_rng(1)
+    b = _rand_bits(rng, (4096,), 3.0)
+    t = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(torch.float64)
+    assert np.array_equal(_f(b), t.numpy())
+
+
+# ---------------------------------------------------------------------------
+# expansion
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
+def test_expand_matches_brute(n):
+    rng = np.random.default_rng(10 + n)
+    V, H, B, L = 37, 6, 2, 9
+    tab = rng.integers(0, 65536, size=(n, V, H), dtype=np.uint16)
+    ids = rng.integers(0, V, size=(B, L))
+    out, bad = oracle.expand_ref(ids, tab)
+    assert not bad
+    ref = brute.brute_expand(ids.tolist(), tab.tolist())
+    assert out.tolist() == ref
+
+
+def test_expand_layout_is_token_major_interleave():
+    rng = np.random.default_rng(3)
+    n, V, H, B, L = 3, 50, 8, 2, 7
+    tab = rng.integers(0, 65536, size=(n, V, H), dtype=np.uint16)
+    ids = rng.integers(0, V, size=(B, L))
+    out, _ = oracle.expand_ref(ids, tab)
+    # [B, L, n, H] view: gather every table at once with fancy indexing
+    want = np.transpose(tab[:, ids], (1, 2, 0, 3)).reshape(B, n * L, H)
+    assert np.array_equal(out, want)
+
+
+def test_expand_n1_is_embedding():
+    rng = np.random.default_rng(4)
+    V, H = 100, 16
+    w = _rand_bits(rng, (1, V, H), 0.02)
+    ids = rng.integers(0, V, size=(3, 11))
+    out, _ = oracle.expand_ref(ids, w)
+    emb = torch.nn.functional.embedding(torch.from_numpy(ids),
+                                        torch.from_numpy(w[0].view(np.int16)))
+    assert np.array_equal(out, emb.numpy().view(np.uint16))
+
+
+def test_expand_out_of_range_ids_zero_and_flag():
+    rng = np.random.default_rng(5)
+    tab = rng.integers(1, 65536, size=(2, 10, 4), dtype=np.uint16)
+    ids = np.array([[0, 10, 3, -1]])
+    out, bad = oracle.expand_ref(ids, tab)
+    assert bad
+    assert np.all(out[0, 2:4] == 0) and np.all(out[0, 6:8] == 0)
+    assert np.array_equal(out[0, 0], tab[0, 0]) and np.array_equal(out[0, 5], tab[1, 3])
+
+
+def test_final_stream_rows_and_cyclic_replication():
+    x = np.arange(2 * 12 * 3).reshape(2, 12, 3)   # n=4, L=3
+    fs = oracle.final_stream_rows_ref(x, 4)
+    assert np.array_equal(fs, x[:, [3, 7, 11]])
+    tab = np.arange(2 * 5 * 3).reshape(2, 5, 3)
+    rep = oracle.cyclic_replicate_ref(tab, 4)
+    assert rep.shape == (4, 5, 3)
+    assert np.array_equal(rep[2], tab[0]) and np.array_equal(rep[3], tab[1])
+
+
+# ---------------------------------------------------------------------------
+# visibility rule: closed forms and the pages' cost orders
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n,L", [(1, 1), (1, 17), (2, 64), (3, 10), (4, 33), (8, 20)])
+def test_pair_count_closed_forms(n, L):
+    N = n * L
+    assert oracle.count_pairs(N, n, WITHIN) == n * L * (L + 1) // 2
+    assert oracle.count_pairs(N, n, MIX) == N * (N + 1) // 2
+
+
+def test_pair_counts_of_the_workloads():
+    # tiny workload (n=2, L=64): closed forms at n*L = 128
+    assert oracle.count_pairs(128, 2, WITHIN) == 4160
+    assert oracle.count_pairs(128, 2, MIX) == 8256
+    # n4 workload (n=4, L=1024)
+    assert oracle.count_pairs(4096, 4, WITHIN) == 2_099_200
+    assert oracle.count_pairs(4096, 4, MIX) == 8_390_656
+
+
+def test_cost_orders_stated_on_the_pages():
+    g = json.load(open(os.path.join(GOLDEN, "cost_orders.json")))
+    n = g["n"]
+    L = 256
+    base = oracle.count_pairs(L, 1, MIX)
+    within = oracle.count_pairs(n * L, n, WITHIN)
+    mix = oracle.count_pairs(n * L, n, MIX)
+    # within-stream cost is exactly the linear reference
+    assert within / base == g["linear_reference_ratio"]
+    # full mixing tends to the dense n^2 figure: n*(nL+1)/(L+1)
+    assert abs(mix / base - g["dense_attention_ratio"]) < g["dense_attention_ratio"] * 0.25 / (L + 1) * n
+    assert mix / base < g["dense_attention_ratio"]
+    # the whole-model costs bracket the linear reference and sit far under dense
+    for r in (g["whole_model_cost_ratio_80B"], g["whole_model_cost_ratio_617B"]):
+        assert g["linear_reference_ratio"] < r < g["dense_attention_ratio"]
+
+
+def test_useful_flops_closed_form():
+    assert oracle.useful_flops(2, 4, 64, 8, 16, WITHIN) == 4 * 16 * 8 * 2 * (4 * 64 * 65 // 2)
+
+
+# ---------------------------------------------------------------------------
+# attention: brute force, library routine, invariants
+# ---------------------------------------------------------------------------
+SHAPES = [
+    # n, L, Hq, Hkv, D
+    (1, 5, 1, 1, 4),
+    (2, 4, 2, 1, 8),
+    (3, 3, 4, 2, 4),
+    (5, 2, 2, 2, 8),
+    (4, 6, 4, 1, 4),
+    (2, 1, 1, 1, 4),
+]
+
+
+def _qkv(rng, B, n, L, Hq, Hkv, D, std=1.0):
+    N = n * L
+    return (_rand_bits(rng, (B, N, Hq, D), std), _rand_bits(rng, (B, N, Hkv, D), std),
+            _rand_bits(rng, (B, N, Hkv, D), std))
+
+
+@pytest.mark.parametrize("n,L,Hq,Hkv,D", SHAPES)
+@pytest.mark.parametrize("mode", [WITHIN, MIX])
+def test_prefill_matches_brute_force(n, L, Hq, Hkv, D, mode):
+    rng = np.random.default_rng(100 + 7 * n + L)
+    q, k, v = _qkv(rng, 2, n, L, Hq, Hkv, D)
+    scale = 0.7
+    got = oracle.prefill_ref(q, k, v, n, mode, scale)
+    ref = np.array(brute.brute_attention(_f(q).tolist(), _f(k).tolist(), _f(v).tolist(),
+                                         n, mode == WITHIN, scale))
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode", [WITHIN, MIX])
+def test_n1_is_ordinary_causal_attention(mode):
+    rng = np.random.default_rng(7)
+    q, k, v = _qkv(rng, 2, 1, 40, 4, 2, 16)
+    got = oracle.prefill_ref(q, k, v, 1, mode, 0.25)
+    ref = _sdpa_causal(_f(q), _f(k), _f(v), 0.25)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("n", [2, 3, 4])
+def test_within_is_n_independent_causal_attentions(n):
+    rng = np.random.default_rng(20 + n)
+    L = 30
+    q, k, v = _qkv(rng, 2, n, L, 4, 2, 16)
+    got = oracle.prefill_ref(q, k, v, n, WITHIN, 0.3)
+    for s in range(n):
+        ref = _sdpa_causal(_f(q[:, s::n]), _f(k[:, s::n]), _f(v[:, s::n]), 0.3)
+        np.testing.assert_allclose(got[:, s::n], ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("n", [2, 3, 8])
+def test_mix_is_causal_attention_over_nL(n):
+    rng = np.random.default_rng(30 + n)
+    q, k, v = _qkv(rng, 1, n, 12, 4, 4, 8)
+    got = oracle.prefill_ref(q, k, v, n, MIX, 0.5)
+    ref = _sdpa_causal(_f(q), _f(k), _f(v), 0.5)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode", [WITHIN, MIX])
+def test_softmax_rows_sum_to_one_and_respect_mask(mode):
+    rng = np.random.default_rng(40)
+    n, L, D = 3, 9, 8
+    N = n * L
+    qf = rng.standard_normal((N, D))
+    kf = rng.standard_normal((N, D))
+    vf = rng.standard_normal((N, D))
+    _, p = oracle.attention_rows(qf, np.arange(N), kf, vf, n, mode, 1.0)
+    assert np.all(np.abs(p.sum(axis=1) - 1.0) < 1e-12)
+    for i in range(N):
+        t, s = divmod(i, n)
+        for j in range(N):
+            t2, s2 = divmod(j, n)
+            if not brute.sees(t, s, t2, s2, mode == WITHIN):
+                assert p[i, j] == 0.0
+            else:
+                assert p[i, j] > 0.0
+
+
+@pytest.mark.parametrize("mode", [WITHIN, MIX])
+def test_v_ones_gives_ones(mode):
+    rng = np.random.default_rng(41)
+    q, k, _ = _qkv(rng, 1, 4, 16, 2, 1, 8, std=2.0)
+    v = np.full(k.shape, 0x3F80, dtype=np.uint16)
+    got = oracle.prefill_ref(q, k, v, 4, mode, 1.0)
+    np.testing.assert_allclose(got, 1.0, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("mode", [WITHIN, MIX])
+def test_k_zero_gives_prefix_means(mode):
+    rng = np.random.default_rng(42)
+    n, L = 3, 11
+    q, _, v = _qkv(rng, 1, n, L, 2, 2, 8)
+    k = np.zeros(v.shape, dtype=np.uint16)
+    got = oracle.prefill_ref(q, k, v, n, mode, 1.0)
+    vf = _f(v)[0]
+    if mode == MIX:
+        want = np.cumsum(vf, axis=0) / np.arange(1, n * L + 1)[:, None, None]
+    else:
+        want = np.empty_like(vf)
+        for s in range(n):
+            want[s::n] = np.cumsum(vf[s::n], axis=0) / np.arange(1, L + 1)[:, None, None]
+    np.testing.assert_allclose(got[0], want, rtol=0, atol=1e-13)
+
+
+def test_stream_one_hot_values_pin_the_within_mask():
+    rng = np.random.default_rng(43)
+    n, L, D = 5, 7, 8
+    q, k, _ = _qkv(rng, 1, n, L, 2, 1, D, std=3.0)
+    v = np.zeros(k.shape, dtype=np.uint16)
+    for i in range(n * L):
+        v[0, i, :, i % n] = 0x3F80
+    got = oracle.prefill_ref(q, k, v, n, WITHIN, 1.0)
+    for i in range(n * L):
+        want = np.zeros(D)
+        want[i % n] = 1.0
+        np.testing.assert_allclose(got[0, i, 0], want, rtol=0, atol=1e-14)
+        np.testing.assert_allclose(got[0, i, 1], want, rtol=0, atol=1e-14)
+
+
+def test_first_token_sees_only_itself():
+    rng = np.random.default_rng(44)
+    n = 4
+    q, k, v = _qkv(rng, 1, n, 5, 4, 2, 8)
+    w = oracle.prefill_ref(q, k, v, n, WITHIN, 1.0)
+    m = oracle.prefill_ref(q, k, v, n, MIX, 1.0)
+    vf = _f(v)
+    for h in range(4):
+        for s in range(n):
+            assert np.array_equal(w[0, s, h], vf[0, s, h // 2])
+        assert np.array_equal(m[0, 0, h], vf[0, 0, h // 2])
+
+
+def test_stream_relabel_equivariance():
+    rng = np.random.default_rng(45)
+    n, L = 4, 6
+    q, k, v = _qkv(rng, 1, n, L, 2, 1, 8)
+    perm = np.array([2, 0, 3, 1])
+
+    def relabel(x):
+        y = x.reshape(x.shape[0], L, n, *x.shape[2:])
+        return y[:, :, perm].reshape(x.shape)
+
+    a = oracle.prefill_ref(relabel(q), relabel(k), relabel(v), n, WITHIN, 1.0)
+    b = relabel(oracle.prefill_ref(q, k, v, n, WITHIN, 1.0))
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-14)
+
+
+def test_row_subset_equals_full():
+    rng = np.random.default_rng(46)
+    n = 3
+    q, k, v = _qkv(rng, 2, n, 20, 4, 2, 8)
+    full = oracle.prefill_ref(q, k, v, n, MIX, 1.0)
+    rows = np.array([0, 7, 31, 59])
+    part = oracle.prefill_ref(q, k, v, n, MIX, 1.0, rows=rows, heads=[1, 3], batches=[1],
+                              chunk=2)
+    np.testing.assert_array_equal(part[0], full[1][rows][:, [1, 3]])
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+def test_decode_append_positions():
+    rng = np.random.default_rng(50)
+    S, n, Hkv, D = 3, 4, 2, 4
+    C = 6 * n
+    kc = rng.integers(0, 65536, size=(S, C, Hkv, D), dtype=np.uint16)
+    vc = rng.integers(0, 65536, size=(S, C, Hkv, D), dtype=np.uint16)
+    kn = rng.integers(0, 65536, size=(S, n, Hkv, D), dtype=np.uint16)
+    vn = rng.integers(0, 65536, size=(S, n, Hkv, D), dtype=np.uint16)
+    tb = np.array([0, 2, 5])
+    k2, v2 = oracle.decode_append_ref(kc, vc, kn, vn, tb, n)
+    for qi in range(S):
+        for e in range(C):
+            t, s = divmod(e, n)
+            if t == tb[qi]:
+                assert np.array_equal(k2[qi, e], kn[qi, s]) and np.array_equal(v2[qi, e], vn[qi, s])
+            else:
+                assert np.array_equal(k2[qi, e], kc[qi, e]) and np.array_equal(v2[qi, e], vc[qi, e])
+
+
+@pytest.mark.parametrize("mode", [WITHIN, MIX])
+def test_decode_equals_prefill_tail(mode):
+    """Decoding token T over a cache of T tokens equals the last n rows of a
+    prefill over T+1 tokens, sequence by sequence (ragged T)."""
+    rng = np.random.default_rng(60 + mode)
+    S, n, Hq, Hkv, D = 3, 3, 4, 2, 8
+    tb = np.array([0, 5, 2])
+    C = 7 * n
+    kc = _rand_bits(rng, (S, C, Hkv, D))
+    vc = _rand_bits(rng, (S, C, Hkv, D))
+    qn = _rand_bits(rng, (S, n, Hq, D))
+    kn = _rand_bits(rng, (S, n, Hkv, D))
+    vn = _rand_bits(rng, (S, n, Hkv, D))
+    k2, v2 = oracle.decode_append_ref(kc, vc, kn, vn, tb, n)
+    got = oracle.decode_ref(qn, k2, v2, tb, n, mode, 0.35)
+    for qi in range(S):
+        T = int(tb[qi])
+        N = (T + 1) * n
+        q = _rand_bits(rng, (1, N, Hq, D))
+        q[0, T * n:] = qn[qi]
+        ref = oracle.prefill_ref(q, k2[qi:qi + 1, :N], v2[qi:qi + 1, :N], n, mode, 0.35)
+        np.testing.assert_allclose(got[qi], ref[0, T * n:], rtol=0, atol=1e-13)
+
+
+def test_decode_matches_brute_force():
+    rng = np.random.default_rng(70)
+    S, n, Hq, Hkv, D, T = 1, 2, 2, 1, 4, 3
+    C = (T + 1) * n
+    kc = _rand_bits(rng, (S, C, Hkv, D))
+    vc = _rand_bits(rng, (S, C, Hkv, D))
+    qn = _rand_bits(rng, (S, n, Hq, D))
+    tb = np.array([T])
+    for mode in (WITHIN, MIX):
+        got = oracle.decode_ref(qn, kc, vc, tb, n, mode, 1.0)
+        q = np.zeros((1, C, Hq, D), dtype=np.uint16)
+        q[0, T * n:] = qn[0]
+        ref = np.array(brute.brute_attention(_f(q).tolist(), _f(kc).tolist(),
+                                             _f(vc).tolist(), n, mode == WITHIN, 1.0))
+        np.testing.assert_allclose(got[0], ref[0, T * n:], rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each must be caught by at least one pin above
+# ---------------------------------------------------------------------------
+def _pins_pass():
+    """Run a compact subset of the pins against the (possibly patched) oracle."""
+    try:
+        test_prefill_matches_brute_force(3, 3, 4, 2, 4, WITHIN)
+        test_prefill_matches_brute_force(3, 3, 4, 2, 4, MIX)
+        test_within_is_n_independent_causal_attentions(3)
+        test_mix_is_causal_attention_over_nL(3)
+        test_pair_count_closed_forms(4, 33)
+        test_decode_equals_prefill_tail(WITHIN)
+    except AssertionError:
+        return False
+    return True
+
+
+def test_planted_mistakes_are_caught(monkeypatch):
+    assert _pins_pass()
+    real = sfa.visible
+
+    def strict(i, j, n, mode):         # forgets the query's own position
+        return real(i, j, n, mode) & (np.asarray(j) != np.asarray(i))
+
+    def no_stream(i, j, n, mode):      # within-stream without the stream test
+        return np.asarray(j) <= np.asarray(i)
+
+    def token_stream(i, j, n, mode):   # stream taken as i // n
+        i, j = np.asarray(i), np.asarray(j)
+        c = j <= i
+        return c & ((j // n) == (i // n)) if mode == WITHIN else c
+
+    def anti(i, j, n, mode):           # causality reversed
+        return real(j, i, n, mode)
+
+    for bad in (strict, no_stream, token_stream, anti):
+        monkeypatch.setattr(sfa, "visible", bad)
+        assert not _pins_pass(), bad.__name__
+        monkeypatch.setattr(sfa, "visible", real)
+
+    real_softmax = sfa._softmax_rows
+
+    def no_norm(s):                    # drops the denominator
+        return np.exp(s - s.max(axis=1, keepdims=True))
+
+    monkeypatch.setattr(sfa, "_softmax_rows", no_norm)
+    assert not _pins_pass()
+    monkeypatch.setattr(sfa, "_softmax_rows", real_softmax)
+
+    real_widen = sfa.bf16_bits_to_f64
+
+    def low_half(bits):                # bf16 bits read as the low half
+        return (np.asarray(bits).astype(np.uint32)).view(np.float32).astype(np.float64)
+
+    monkeypatch.setattr(sfa, "bf16_bits_to_f64", low_half)
+    try:
+        test_bf16_known_values()
+        caught = False
+    except AssertionError:
+        caught = True
+    monkeypatch.setattr(sfa, "bf16_bits_to_f64", real_widen)
+    assert caught
+    assert _pins_pass()
