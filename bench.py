@@ -1,0 +1,332 @@
+#!/usr/bin/env python3
+"""Benchmark of the SFA hot path on one MI355X.
+
+One step = one pass of the prefill hot path over the n=4 workload
+(n=4, B=2, L=1024 -> nL=4096, 32 query / 8 KV heads, D=128, bf16):
+    hd_expand (vocab 151936, hidden 4096)  ->  within-stream layer  ->  mixing layer.
+``value`` is useful attention TFLOP/s of the step (4*D FLOPs per visible
+(query, key) pair per query head; the expansion moves bytes, no FLOPs).
+
+Also reported on the same JSON line:
+  roofline      the prefill attention kernel against the bf16 MFMA peak,
+                timed with HIP events on the stream it runs on;
+  kernels       per-kernel times and rooflines (expansion and decode: HBM);
+  decode        the decode step (64 sequences x 16384 cached entries, n=4,
+                32/8 heads) in both modes: useful GB/s against HBM peak;
+  stack         n=8, L=2048 stack (3 within + 1 mixing) vs the n=1 stack;
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same
+                workload, on the host cores (a reported baseline only).
+
+Inputs are resident in HBM before the timed region starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SFA attention useful TFLOP/s (prefill) and GB/s (decode), % of MI355X roofline"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def pairs(n, L, mode):
+    """Visible (query, key) pairs per (batch, head): n*L*(L+1)/2 within-stream,
+    N*(N+1)/2 mixing (N = n*L)."""
+    N = n * L
+    return n * L * (L + 1) // 2 if mode == "within" else N * (N + 1) // 2
+
+
+def attn_flops(B, n, L, Hq, D, mode):
+    return 4 * D * Hq * B * pairs(n, L, mode)
+
+
+def decode_bytes(S, n, T, Hkv, D):
+    """K+V bytes of the whole live cache (T+1 tokens x n streams) per call."""
+    return S * (T + 1) * n * Hkv * D * 2 * 2
+
+
+def _events(k):
+    import torch
+    return [torch.cuda.Event(enable_timing=True) for _ in range(k)]
+
+
+def bench_prefill(args, torch, hd, si):
+    cfg = si.N4
+    dev = torch.device("cuda")
+    ids, tab = si.expand_inputs(cfg, device=dev)
+    q, k, v = si.prefill_qkv(cfg, device=dev)
+    x = torch.empty((cfg.B, cfg.N, cfg.hidden), dtype=torch.bfloat16, device=dev)
+    ow = torch.empty_like(q)
+    om = torch.empty_like(q)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        hd.expand(ids, tab, out=x)
+        if ev: ev[1].record()
+        hd.stream_attn(q, k, v, cfg.n, cfg.scale, out=ow)
+        if ev: ev[2].record()
+        hd.mix_attn(q, k, v, cfg.n, cfg.scale, out=om)
+        if ev: ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # whole-step timing: K steps back to back, no events inside
+    t0, t1 = _events(2)
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    # per-kernel timing: events around each launch on the same stream
+    evs = [_events(4) for _ in range(args.steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    t_exp = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    t_w = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    t_m = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+
+    fw = attn_flops(cfg.B, cfg.n, cfg.L, cfg.Hq, cfg.D, "within")
+    fm = attn_flops(cfg.B, cfg.n, cfg.L, cfg.Hq, cfg.D, "mix")
+    exp_bytes = cfg.B * cfg.N * cfg.hidden * 2 * 2 + cfg.B * cfg.L * 4
+    res = dict(cfg=cfg, ms_step=ms_step, t_exp=t_exp, t_w=t_w, t_m=t_m, fw=fw, fm=fm,
+               exp_bytes=exp_bytes)
+    del ids, tab, q, k, v, x, ow, om
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode(args, torch, hd, si):
+    cfg = si.DECODE
+    dev = torch.device("cuda")
+    qn, kn, vn, kc, vc, tb = si.decode_inputs(cfg, device=dev)
+    ws = torch.empty(hd.decode_workspace_size(cfg.S, cfg.n, cfg.Hq, cfg.Hkv, cfg.D, cfg.T),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty_like(qn)
+    reps = max(3, args.steps // 2)
+    res = {}
+    for mode, name in ((0, "within"), (1, "mix")):
+        for _ in range(2):
+            hd.decode_step(qn, kn, vn, kc, vc, tb, cfg.n, cfg.T, mode, cfg.scale, ws, out)
+        torch.cuda.synchronize()
+        e0, e1 = _events(2)
+        e0.record()
+        for _ in range(reps):
+            hd.decode_step(qn, kn, vn, kc, vc, tb, cfg.n, cfg.T, mode, cfg.scale, ws, out)
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / reps
+    res["bytes"] = decode_bytes(cfg.S, cfg.n, cfg.T, cfg.Hkv, cfg.D)
+    res["cfg"] = cfg
+    del qn, kn, vn, kc, vc, tb, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_stack(args, torch, hd, si):
+    """n=8, L=2048 stack of 3 within + 1 mixing layers vs the n=1 stack
+    (4 causal layers at L=2048, same heads)."""
+    cfg = si.N8STACK
+    dev = torch.device("cuda")
+    layers = [si.prefill_qkv(cfg, layer=i, device=dev) for i in range(4)]
+    base = [si.prefill_qkv(cfg, layer=i, device=dev, B=1, L=cfg.L // 1) for i in range(4)]
+    base = [(q[:, :cfg.L].contiguous(), k[:, :cfg.L].contiguous(), v[:, :cfg.L].contiguous())
+            for q, k, v in base]
+    out = torch.empty_like(layers[0][0])
+    out1 = torch.empty_like(base[0][0])
+    reps = max(2, args.steps // 4)
+
+    def run_hd():
+        for i, (q, k, v) in enumerate(layers):
+            fn = hd.mix_attn if cfg.layers[i] == "mix" else hd.stream_attn
+            fn(q, k, v, cfg.n, cfg.scale, out=out)
+
+    def run_base():
+        for q, k, v in base:
+            hd.mix_attn(q, k, v, 1, cfg.scale, out=out1)
+
+    def timeit(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = _events(2)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    t_hd = timeit(run_hd)
+    t_base = timeit(run_base)
+    q, k, v = layers[0]
+    t_w = timeit(lambda: hd.stream_attn(q, k, v, cfg.n, cfg.scale, out=out))
+    t_m = timeit(lambda: hd.mix_attn(q, k, v, cfg.n, cfg.scale, out=out))
+    fl_hd = 3 * attn_flops(1, cfg.n, cfg.L, cfg.Hq, cfg.D, "within") + \
+        attn_flops(1, cfg.n, cfg.L, cfg.Hq, cfg.D, "mix")
+    fl_base = 4 * attn_flops(1, 1, cfg.L, cfg.Hq, cfg.D, "mix")
+    del layers, base, out, out1
+    torch.cuda.empty_cache()
+    return {
+        "workload": "n=8 B=1 L=2048 (nL=16384) Hq=32 Hkv=8 D=128; 3 within + 1 mixing layer "
+                    "vs n=1 stack of 4 causal layers at L=2048",
+        "ms_stack": round(t_hd, 4), "ms_stack_n1": round(t_base, 4),
+        "time_ratio_vs_n1": round(t_hd / t_base, 3), "flop_ratio_vs_n1": round(fl_hd / fl_base, 3),
+        "ms_within": round(t_w, 4), "ms_mix": round(t_m, 4),
+        "mix_over_within_time": round(t_m / t_w, 3),
+        "mix_over_within_flops": round(attn_flops(1, cfg.n, cfg.L, cfg.Hq, cfg.D, "mix") /
+                                       attn_flops(1, cfg.n, cfg.L, cfg.Hq, cfg.D, "within"), 3),
+        "stack_tflops": round(fl_hd / (t_hd * 1e-3) / 1e12, 2),
+    }
+
+
+def cpu_baseline(si, budget_s):
+    """Oracle on a bounded sample of the n=4 workload: the last query rows of
+    batch 0 (the most expensive ones), all 32 heads, both layers, growing the
+    sample until ``budget_s`` seconds of CPU work have been spent."""
+    import numpy as np
+    import oracle
+    cfg = si.N4
+    q, k, v = si.prefill_qkv(cfg, B=1)
+    qb, kb, vb = si.bits(q), si.bits(k), si.bits(v)
+    N = cfg.N
+    flops = 0
+    rows_done = 0
+    t0 = time.perf_counter()
+    block = 64
+    while time.perf_counter() - t0 < budget_s and rows_done < N:
+        hi = N - rows_done
+        rows = np.arange(hi - block, hi)
+        for mode in (oracle.WITHIN, oracle.MIX):
+            oracle.prefill_ref(qb, kb, vb, cfg.n, mode, cfg.scale, rows=rows)
+            keys = (rows // cfg.n + 1) if mode == oracle.WITHIN else (rows + 1)
+            flops += 4 * cfg.D * cfg.Hq * int(keys.sum())
+        rows_done += block
+    dt = time.perf_counter() - t0
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:
+        threads = os.cpu_count()
+    return {
+        "value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+        "kind": "oracle",
+        "sample": f"n4 workload, batch 0, all 32 heads, last {rows_done} query rows of the "
+                  f"4096 (within-stream and mixing layers), float64 NumPy oracle, "
+                  f"{dt:.1f} s wall, {flops / 1e9:.2f} useful GFLOP",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of CPU oracle work for cpu_baseline (0 to skip)")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-stack", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the SFA hot path on a single "
+              "MI355X (no collectives); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sequence_length_latent_amd as hd
+    import sfa_inputs as si
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    hd.load()
+
+    pf = bench_prefill(args, torch, hd, si)
+    print(f"[bench] prefill done: step {pf['ms_step']:.4f} ms", file=sys.stderr, flush=True)
+    dec = None if args.no_decode else bench_decode(args, torch, hd, si)
+    if dec:
+        print(f"[bench] decode done: within {dec['within']:.4f} ms mix {dec['mix']:.4f} ms",
+              file=sys.stderr, flush=True)
+    stack = None if args.no_stack else bench_stack(args, torch, hd, si)
+    if stack:
+        print("[bench] stack done", file=sys.stderr, flush=True)
+    cpu = None
+    if args.cpu_budget > 0:
+        cpu = cpu_baseline(si, args.cpu_budget)
+        print("[bench] cpu baseline done", file=sys.stderr, flush=True)
+
+    cfg = pf["cfg"]
+    flops = pf["fw"] + pf["fm"]
+    value = flops / (pf["ms_step"] * 1e-3) / 1e12
+    attn_ms = pf["t_w"] + pf["t_m"]
+    ach = flops / (attn_ms * 1e-3) / 1e12
+    kernels = {
+        "hd_expand": {"ms": round(pf["t_exp"], 4), "bound": "hbm",
+                      "achieved": round(pf["exp_bytes"] / (pf["t_exp"] * 1e-3) / 1e9, 1),
+                      "unit": "GB/s", "peak": PEAK_HBM_GBS},
+        "sfa_stream_attn": {"ms": round(pf["t_w"], 4), "bound": "mfma",
+                            "achieved": round(pf["fw"] / (pf["t_w"] * 1e-3) / 1e12, 2),
+                            "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS},
+        "sfa_mix_attn": {"ms": round(pf["t_m"], 4), "bound": "mfma",
+                         "achieved": round(pf["fm"] / (pf["t_m"] * 1e-3) / 1e12, 2),
+                         "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS},
+    }
+    for kk in kernels.values():
+        kk["frac"] = round(kk["achieved"] / kk["peak"], 4)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pf["ms_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "n4: n=4 streams, batch 2, L=1024 tokens (nL=4096), 32 query / 8 KV "
+                        "heads, head_dim 128; step = hd_expand (vocab 151936, hidden 4096) + "
+                        "within-stream layer + mixing layer",
+            "n": cfg.n, "batch": cfg.B, "L": cfg.L, "nL": cfg.N, "Hq": cfg.Hq, "Hkv": cfg.Hkv,
+            "head_dim": cfg.D, "useful_gflop_per_step": round(flops / 1e9, 3),
+        },
+        "roofline": {
+            "kernel": "sfa_prefill_kernel<128> (both layers; 2 launches per step)",
+            "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+        },
+        "kernels": kernels,
+    }
+    if dec:
+        line["decode"] = {
+            "workload": "64 sequences x 4096 tokens x 4 streams cached (16388 live entries after "
+                        "the append), 32/8 heads, head_dim 128; one decode step = append + "
+                        "attention + split combine",
+            "bytes_per_call": dec["bytes"],
+        }
+        for name in ("within", "mix"):
+            gbs = dec["bytes"] / (dec[name] * 1e-3) / 1e9
+            line["decode"][name] = {"ms": round(dec[name], 4), "achieved": round(gbs, 1),
+                                    "unit": "GB/s", "peak": PEAK_HBM_GBS,
+                                    "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    if stack:
+        line["stack"] = stack
+    line["cpu_baseline"] = cpu
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

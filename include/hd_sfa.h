@@ -1,0 +1,165 @@
+/*
+ * hd_sfa.h -- C ABI of the MI355X (gfx950) Stream-Factorized Attention library.
+ *
+ * Hidden Decoding expands every token into n streams, each drawn from its own
+ * embedding table, and runs the unchanged backbone over the resulting length-nL
+ * sequence.  Most attention layers read only their own stream; a few mixing
+ * layers use the base model's full causal pattern over the whole sequence; the
+ * KV of every stream is kept so later tokens read it as context.  Sources:
+ * "Hidden Decoding at Scale" review (romaanj.github.io), section Method; the
+ * arXiv 2607.08186 abstract; the Tencent/Sequential-Hidden-Decoding README,
+ * section Key Idea.
+ *
+ * Conventions shared by every entry point
+ *   - Expanded position of (token t, stream s) is p = t*n + s (token-major,
+ *     stream 0 first).  Table s feeds stream s.
+ *   - All tensors are dense, row-major, contiguous, and live in device memory
+ *     unless a parameter says otherwise.  bf16 values are passed as their
+ *     16-bit patterns (uint16_t).  Pointers to bf16 data must be 16-byte
+ *     aligned.
+ *   - Query head h reads KV head h / (Hq / Hkv).
+ *   - Every call is asynchronous on `stream` (NULL = the null stream), keeps
+ *     no state between calls, never synchronises, and allocates nothing: the
+ *     caller owns every buffer and the stream.
+ *   - Arguments are validated on the host before anything is launched; an
+ *     invalid call returns a non-zero hd_status and touches no memory.  Data
+ *     that only the device can check (token ids) is reported through a device
+ *     flag.  No C++ exception crosses this interface.
+ *   - A call whose total work is zero (B, L or S equal to 0) returns HD_OK
+ *     without launching.
+ */
+#ifndef HD_SFA_H
+#define HD_SFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum hd_status {
+    HD_OK = 0,
+    HD_ERR_NULL = 1,         /* a required pointer is NULL                       */
+    HD_ERR_SHAPE = 2,        /* a size is negative/zero where it must not be,
+                                Hq is not a multiple of Hkv, or a pointer is
+                                misaligned                                        */
+    HD_ERR_UNSUPPORTED = 3,  /* head_dim other than 64/128, or a size beyond the
+                                library's 32-bit index range                     */
+    HD_ERR_CAPACITY = 4,     /* KV cache too small for the appended entries      */
+    HD_ERR_LAUNCH = 5,       /* the HIP runtime refused a launch                 */
+    HD_ERR_WORKSPACE = 6     /* decode workspace NULL or smaller than required   */
+} hd_status;
+
+/* Static, NUL-terminated description of a status code; never NULL. */
+const char* hd_status_string(int status);
+
+/* Version of this interface (incremented on any signature change). */
+int hd_abi_version(void);
+
+/*
+ * hd_expand -- embedding expansion and interleave.
+ * Review, section Method ("n streams with independent embedding tables",
+ * "length-nL sequence"); README, section Key Idea, items 1 and 2.
+ *
+ *   out[b, t*n + s, :] = tables[s, ids[b, t], :]   for b < B, t < L, s < n
+ *
+ *   ids      int32 [B, L]           token ids
+ *   tables   bf16  [n, V, H]        n stacked independent tables
+ *   out      bf16  [B, n*L, H]      written in full
+ *   err_flag int32 scalar or NULL   if not NULL and some id lies outside
+ *                                   [0, V), *err_flag is set to 1 (it is never
+ *                                   cleared: the caller zeroes it first); the n
+ *                                   rows of such a token are written as zeros
+ * Pure copy: the result is bit-identical to the gather.  H must be a multiple
+ * of 8.
+ */
+hd_status hd_expand(const int32_t* ids, int64_t B, int64_t L,
+                    const uint16_t* tables, int32_t n, int64_t V, int64_t H,
+                    uint16_t* out, int32_t* err_flag, hipStream_t stream);
+
+/*
+ * sfa_stream_attn -- within-stream causal attention over the expanded
+ * sequence (prefill).  Review, section Method: most layers attend only within
+ * their own stream, at a cost of order n*L^2.
+ *
+ *   O[b, p(t,s), h] = sum over t' <= t of
+ *       softmax_t'( scale * q[b,p(t,s),h] . k[b,p(t',s),g] ) v[b,p(t',s),g]
+ *
+ *   q, out   bf16 [B, n*L, Hq, D]
+ *   k, v     bf16 [B, n*L, Hkv, D]
+ *   D        64 or 128; Hq a multiple of Hkv
+ * Scores, softmax statistics and the output accumulator are fp32; the two
+ * contractions run on bf16 matrix cores; out is rounded to nearest even.
+ * Work skipped: only token tiles of the query's own stream that are not in
+ * its future are visited, so the cost grows linearly in n.
+ */
+hd_status sfa_stream_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                          uint16_t* out, int64_t B, int32_t n, int64_t L,
+                          int32_t Hq, int32_t Hkv, int32_t D, float softmax_scale,
+                          hipStream_t stream);
+
+/*
+ * sfa_mix_attn -- mixing attention, full causal pattern over the interleaved
+ * length-nL order (prefill).  Review, section Method: a few layers mix
+ * streams following the base model's own (full) attention pattern, reading
+ * the retained intermediate-stream KV.
+ *
+ *   O[b, i, h] = sum over j <= i of softmax_j(scale * q[b,i,h] . k[b,j,g]) v[b,j,g]
+ *
+ * Same arguments, layouts, precision and errors as sfa_stream_attn.
+ */
+hd_status sfa_mix_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                       uint16_t* out, int64_t B, int32_t n, int64_t L,
+                       int32_t Hq, int32_t Hkv, int32_t D, float softmax_scale,
+                       hipStream_t stream);
+
+/*
+ * sfa_decode_workspace_size -- bytes of device workspace sfa_decode_step
+ * needs for these sizes (fp32 split partials).  Returns 0 for invalid sizes.
+ */
+size_t sfa_decode_workspace_size(int64_t S, int32_t n, int32_t Hq, int32_t Hkv,
+                                 int32_t D, int64_t max_tokens);
+
+/*
+ * sfa_decode_step -- one decode step of Hidden Decoding for S sequences.
+ * Review, sections Method and Limitations: every stream's KV is retained, so
+ * the cache holds n entries per token and decode reads all of them; the
+ * review's Notes: small-batch decode is bandwidth-bound.
+ *
+ * 1. Append: for each sequence q with T = tokens_before[q],
+ *      k_cache[q, T*n + s] = k_new[q, s],  v_cache likewise   (s < n)
+ *    (idempotent: calling twice with the same inputs writes the same bytes).
+ * 2. Attention of the n new queries (T, s) of every sequence:
+ *      mode 0 (within-stream): keys t'*n + s for t' <= T
+ *      mode 1 (mixing):        every entry j <= T*n + s
+ *
+ *   q_new          bf16 [S, n, Hq, D]
+ *   k_new, v_new   bf16 [S, n, Hkv, D]
+ *   k_cache, v_cache bf16 [S, C_max, Hkv, D], entry order p = t*n + s
+ *   tokens_before  int32 [S], device memory, 0 <= T <= max_tokens
+ *                  (values outside that range are clamped into it on the
+ *                  device, so no access leaves the cache)
+ *   max_tokens     host-side bound on tokens_before, sizes the grid
+ *   C_max          must be >= (max_tokens + 1) * n, else HD_ERR_CAPACITY
+ *   workspace      device scratch of at least sfa_decode_workspace_size()
+ *                  bytes, else HD_ERR_WORKSPACE; contents need no init
+ *   out            bf16 [S, n, Hq, D]
+ * Requires n * Hq / Hkv <= 64 query rows per KV head.
+ */
+hd_status sfa_decode_step(const uint16_t* q_new, const uint16_t* k_new,
+                          const uint16_t* v_new, uint16_t* k_cache,
+                          uint16_t* v_cache, const int32_t* tokens_before,
+                          int64_t S, int32_t n, int32_t Hq, int32_t Hkv,
+                          int32_t D, int64_t C_max, int64_t max_tokens,
+                          int32_t mode, float softmax_scale, void* workspace,
+                          size_t workspace_bytes, uint16_t* out,
+                          hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HD_SFA_H */

@@ -1,0 +1,137 @@
+"""Python binding of the MI355X Stream-Factorized Attention library.
+
+Thin argument marshalling over the C ABI in ``include/hd_sfa.h``: each function
+checks dtype / device / contiguity / shape of its torch tensors, passes raw
+device pointers and the current HIP stream, and raises ``HDError`` on a
+non-zero status.  Every step of the computation runs in the library's HIP
+kernels; PyTorch only provides device memory and the stream.
+
+Expanded position of (token t, stream s) is t*n + s; query head h reads KV
+head h // (Hq // Hkv).
+"""
+from __future__ import annotations
+
+import torch
+
+from ._lib import HDError, check, load  # noqa: F401
+
+__all__ = ["expand", "stream_attn", "mix_attn", "decode_workspace_size", "decode_step",
+           "HDError", "load", "WITHIN", "MIX"]
+
+WITHIN = 0
+MIX = 1
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def expand(ids: torch.Tensor, tables: torch.Tensor, out: torch.Tensor | None = None,
+           err_flag: torch.Tensor | None = None) -> torch.Tensor:
+    """out[b, t*n+s, :] = tables[s, ids[b, t], :].  ids int32 [B, L],
+    tables bf16 [n, V, H] -> out bf16 [B, n*L, H].  ``err_flag`` (int32, one
+    element, zeroed by the caller) is set to 1 if an id is out of range."""
+    _need(ids, "ids", torch.int32, 2)
+    _need(tables, "tables", torch.bfloat16, 3)
+    B, L = ids.shape
+    n, V, H = tables.shape
+    if out is None:
+        out = torch.empty((B, n * L, H), dtype=torch.bfloat16, device=tables.device)
+    _need(out, "out", torch.bfloat16, 3)
+    if tuple(out.shape) != (B, n * L, H):
+        raise ValueError(f"out must be {(B, n * L, H)}")
+    flag = 0
+    if err_flag is not None:
+        _need(err_flag, "err_flag", torch.int32, 1)
+        flag = err_flag.data_ptr()
+    st = load().hd_expand(ids.data_ptr(), B, L, tables.data_ptr(), n, V, H, out.data_ptr(),
+                          flag or None, _stream())
+    check("hd_expand", st)
+    return out
+
+
+def _attn(fn_name: str, q, k, v, n: int, scale: float, out):
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if n < 1 or N % n:
+        raise ValueError(f"sequence length {N} is not a multiple of n={n}")
+    if tuple(k.shape) != (B, N, Hkv, D) or tuple(v.shape) != (B, N, Hkv, D):
+        raise ValueError("k and v must be [B, n*L, Hkv, D] matching q")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, 4)
+    if out.shape != q.shape:
+        raise ValueError("out must match q")
+    st = getattr(load(), fn_name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                  B, n, N // n, Hq, Hkv, D, float(scale), _stream())
+    check(fn_name, st)
+    return out
+
+
+def stream_attn(q, k, v, n: int, scale: float, out=None):
+    """Within-stream causal attention.  q [B, n*L, Hq, D], k/v [B, n*L, Hkv, D]."""
+    return _attn("sfa_stream_attn", q, k, v, n, scale, out)
+
+
+def mix_attn(q, k, v, n: int, scale: float, out=None):
+    """Mixing attention: full causal over the interleaved n*L order."""
+    return _attn("sfa_mix_attn", q, k, v, n, scale, out)
+
+
+def decode_workspace_size(S: int, n: int, Hq: int, Hkv: int, D: int, max_tokens: int) -> int:
+    return int(load().sfa_decode_workspace_size(S, n, Hq, Hkv, D, max_tokens))
+
+
+def decode_step(q_new, k_new, v_new, k_cache, v_cache, tokens_before, n: int,
+                max_tokens: int, mode: int, scale: float, workspace=None, out=None):
+    """Append the n new stream positions and attend from them (mode WITHIN or
+    MIX).  q_new [S, n, Hq, D]; k_new/v_new [S, n, Hkv, D]; caches
+    [S, C, Hkv, D] (appended in place); tokens_before int32 [S] on the GPU."""
+    _need(q_new, "q_new", torch.bfloat16, 4)
+    _need(k_new, "k_new", torch.bfloat16, 4)
+    _need(v_new, "v_new", torch.bfloat16, 4)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    _need(tokens_before, "tokens_before", torch.int32, 1)
+    S, n_, Hq, D = q_new.shape
+    if n_ != n:
+        raise ValueError("q_new must be [S, n, Hq, D]")
+    Hkv = k_new.shape[2]
+    C = k_cache.shape[1]
+    if tuple(k_new.shape) != (S, n, Hkv, D) or tuple(v_new.shape) != (S, n, Hkv, D):
+        raise ValueError("k_new/v_new must be [S, n, Hkv, D]")
+    if tuple(k_cache.shape) != (S, C, Hkv, D) or tuple(v_cache.shape) != (S, C, Hkv, D):
+        raise ValueError("caches must be [S, C, Hkv, D]")
+    if tuple(tokens_before.shape) != (S,):
+        raise ValueError("tokens_before must be [S]")
+    need = decode_workspace_size(S, n, Hq, Hkv, D, max_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_new.device)
+    if out is None:
+        out = torch.empty_like(q_new)
+    _need(out, "out", torch.bfloat16, 4)
+    if out.shape != q_new.shape:
+        raise ValueError("out must match q_new")
+    st = load().sfa_decode_step(q_new.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                                k_cache.data_ptr(), v_cache.data_ptr(), tokens_before.data_ptr(),
+                                S, n, Hq, Hkv, D, C, max_tokens, int(mode), float(scale),
+                                workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                out.data_ptr(), _stream())
+    check("sfa_decode_step", st)
+    return out

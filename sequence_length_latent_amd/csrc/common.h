@@ -1,0 +1,51 @@
+// Internal helpers shared by the HIP sources of the SFA library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hd_sfa.h"
+
+namespace hdsfa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// log2(e): the softmax is evaluated as exp2(s * scale * log2(e) - m).
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Round-to-nearest-even float -> bf16 pair packed in one 32-bit word
+// (lo in bits 0..15).  The compiler lowers the __bf16 conversion to the
+// hardware convert on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    __bf16 a = (__bf16)lo;
+    __bf16 b = (__bf16)hi;
+    uint16_t ua = __builtin_bit_cast(uint16_t, a);
+    uint16_t ub = __builtin_bit_cast(uint16_t, b);
+    return (uint32_t)ua | ((uint32_t)ub << 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) {
+    return __builtin_amdgcn_exp2f(x);
+}
+
+// Exchange with the lane 32 positions away (the other half of the wave).
+__device__ __forceinline__ float xor32(float x) {
+    return __shfl_xor(x, 32, kWave);
+}
+
+inline bool aligned16(const void* p) {
+    return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+inline hd_status launch_status() {
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? HD_OK : HD_ERR_LAUNCH;
+}
+
+}  // namespace hdsfa

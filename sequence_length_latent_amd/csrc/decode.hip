@@ -1,0 +1,510 @@
+// Hidden Decoding decode step over the retained per-stream KV cache
+// (sfa_decode_workspace_size, sfa_decode_step).
+//
+// "Hidden Decoding at Scale" review, sections Method and Limitations: the KV
+// of every stream is kept, so the cache holds n entries per token and later
+// tokens read all of them; section Notes: small-batch decode is bound by
+// memory bandwidth.  Each step appends the n new stream positions of the next
+// token and attends from them.
+//
+// Three kernels on the caller's stream:
+//   1. append   -- copies k_new/v_new into entries T*n .. T*n+n-1;
+//   2. attend   -- split-K over a strided view of the cache.  Within-stream
+//                  mode: one view per stream s (entries s, s+n, ..., T*n+s),
+//                  whose G query rows all sit at its last entry, so no mask
+//                  is needed.  Mixing mode: one view of all (T+1)*n entries
+//                  with n*G query rows, causal only among the n new entries.
+//                  Either way every cache byte is read exactly once per call.
+//                  K and V tiles are staged through LDS with coalesced loads
+//                  (V transposed for the V^T operand) and both contractions
+//                  run on v_mfma_f32_32x32x16_bf16; 4 waves take 32 keys each
+//                  of a 128-key tile and merge their (max, sum, O) at the end;
+//   3. combine  -- merges the per-split partials (fp32) into bf16 output.
+// No atomics: results are bitwise reproducible run to run.
+#include "common.h"
+
+namespace hdsfa {
+
+namespace {
+
+constexpr int DT = 128;            // keys per workgroup tile (32 per wave)
+constexpr int DNW = 4;             // waves
+constexpr int DTHREADS = DNW * kWave;
+constexpr int DVP = DT + 8;        // transposed-V pitch (elements)
+constexpr int kTargetBlocks = 2048;
+
+struct DecodeArgs {
+    const uint16_t* q;         // [S, n, Hq, D]
+    const uint16_t* kc;        // [S, C, Hkv, D]
+    const uint16_t* vc;
+    const int32_t* tokens_before;
+    float* ws;
+    uint64_t cache_seq;        // C * Hkv * D
+    uint32_t n, Hq, Hkv, G, R; // R = n*G query rows per KV head
+    uint32_t max_tokens;
+    uint32_t nsplit, split;    // splits per view, keys per split (multiple of DT)
+    uint32_t within;
+    float c;
+};
+
+__device__ __forceinline__ int vt_pos(int kq) {
+    const int qq = kq & 3;
+    return 16 * (kq >> 2) + ((qq & 1) << 3) + ((qq >> 1) << 2);
+}
+
+__device__ __forceinline__ uint32_t clamp_tokens(int32_t t, uint32_t max_tokens) {
+    return t < 0 ? 0u : ((uint32_t)t > max_tokens ? max_tokens : (uint32_t)t);
+}
+
+// ---------------------------------------------------------------------------
+// 1. append
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+decode_append_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new,
+                     u32x4* __restrict__ kc, u32x4* __restrict__ vc,
+                     const int32_t* __restrict__ tokens_before, uint32_t S, uint32_t n,
+                     uint32_t row_chunks /* Hkv*D/8 */, uint64_t cache_seq_chunks,
+                     uint32_t max_tokens) {
+    const uint32_t idx = blockIdx.x * 256 + threadIdx.x;
+    const uint32_t per_seq = n * row_chunks;
+    if (idx >= S * per_seq) return;
+    const uint32_t seq = idx / per_seq;
+    const uint32_t rem = idx - seq * per_seq;      // s*row_chunks + w
+    const uint32_t T = clamp_tokens(tokens_before[seq], max_tokens);
+    const uint64_t dst = seq * cache_seq_chunks + (uint64_t)T * n * row_chunks + rem;
+    kc[dst] = k_new[idx];
+    vc[dst] = v_new[idx];
+}
+
+// ---------------------------------------------------------------------------
+// 2. split-K attention
+// ---------------------------------------------------------------------------
+template <int D, int NQB>
+__global__ void __launch_bounds__(DTHREADS) __attribute__((amdgpu_waves_per_eu(1, 2)))
+decode_attend_kernel(const DecodeArgs a) {
+    constexpr int KP = D + 8;
+    constexpr int KS_ELEMS = DT * KP;
+    constexpr int DSTEPS = D / 16;
+    constexpr int DBLK = D / 32;
+    constexpr int CPR = D / 8;
+    constexpr int K_CHUNKS = DT * CPR / DTHREADS;
+    constexpr int V_TASKS = (DT / 4) * (D / 8);
+    constexpr int V_PER = V_TASKS / DTHREADS;
+    static_assert(V_TASKS % DTHREADS == 0, "tile/thread mismatch");
+    // LDS: K tile + transposed V tile; reused for the cross-wave merge
+    constexpr int TILE_ELEMS = KS_ELEMS + D * DVP;
+    constexpr int MERGE_FLOATS = DNW * NQB * 32 * D;
+    constexpr int SMEM_BYTES = (TILE_ELEMS * 2 > MERGE_FLOATS * 4) ? TILE_ELEMS * 2 : MERGE_FLOATS * 4;
+    __shared__ __attribute__((aligned(16))) unsigned char smem_raw[SMEM_BYTES];
+    __shared__ float sm_m[DNW][NQB * 32];
+    __shared__ float sm_l[DNW][NQB * 32];
+    uint16_t* ks = reinterpret_cast<uint16_t*>(smem_raw);
+    uint16_t* vt = ks + KS_ELEMS;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int l32 = lane & 31;
+    const int hh = lane >> 5;
+
+    const uint32_t sp = blockIdx.x;
+    const uint32_t views = a.within ? a.n : 1u;
+    const uint32_t view = blockIdx.y % views;
+    const uint32_t kvh = blockIdx.y / views;
+    const uint32_t seq = blockIdx.z;
+
+    const uint32_t T = clamp_tokens(a.tokens_before[seq], a.max_tokens);
+    const uint32_t len = a.within ? T + 1 : (T + 1) * a.n;     // keys in the view
+    const uint32_t key0 = sp * a.split;
+    if (key0 >= len) return;                                    // whole block idle
+    const uint32_t key_end = min(len, key0 + a.split);
+    const int n_tiles = (int)((key_end - key0 + DT - 1) / DT);
+
+    // view rows: key index i of the view is cache entry i*rstride + view
+    const uint32_t rstride = a.within ? a.n : 1u;
+    const uint64_t erow = (uint64_t)a.Hkv * D;                  // elements per cache entry
+    const uint16_t* kbase = a.kc + seq * a.cache_seq + (uint64_t)view * erow + (uint64_t)kvh * D;
+    const uint16_t* vbase = a.vc + seq * a.cache_seq + (uint64_t)view * erow + (uint64_t)kvh * D;
+    const uint64_t kstep = (uint64_t)rstride * erow;
+
+    // query rows of this view: within -> the G heads of stream `view`;
+    // mixing -> r = s*G + gh for every stream s.
+    const uint32_t rows = a.within ? a.G : a.R;
+    bf16x8 qf[NQB][DSTEPS];
+    uint32_t qidx[NQB];                                          // last visible key
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        const uint32_t rl = qb * 32 + l32;
+        const bool ok = rl < rows;
+        const uint32_t r = a.within ? view * a.G + rl : rl;
+        const uint32_t s = r / a.G;
+        const uint32_t gh = r - s * a.G;
+        qidx[qb] = a.within ? T : T * a.n + s;
+        const u32x4* src = reinterpret_cast<const u32x4*>(
+            a.q + (((uint64_t)seq * a.n + s) * a.Hq + kvh * a.G + gh) * D);
+#pragma unroll
+        for (int e = 0; e < DSTEPS; ++e) {
+            u32x4 w = ok ? src[2 * e + hh] : u32x4{0u, 0u, 0u, 0u};
+            qf[qb][e] = __builtin_bit_cast(bf16x8, w);
+        }
+    }
+
+    f32x16 oacc[NQB][DBLK];
+    float m_run[NQB], l_run[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        m_run[qb] = -INFINITY;
+        l_run[qb] = 0.f;
+#pragma unroll
+        for (int i = 0; i < DBLK; ++i) oacc[qb][i] = f32x16{};
+    }
+
+    u32x4 kreg[K_CHUNKS];
+    u32x4 vreg[V_PER][4];
+    auto load_tile = [&](int t) {
+        const uint32_t k0 = key0 + (uint32_t)t * DT;
+#pragma unroll
+        for (int i = 0; i < K_CHUNKS; ++i) {
+            const int cidx = tid + i * DTHREADS;
+            const int row = cidx / CPR;
+            const int col = cidx % CPR;
+            const uint32_t key = k0 + row;
+            kreg[i] = key < key_end
+                ? *reinterpret_cast<const u32x4*>(kbase + key * kstep + col * 8)
+                : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < V_PER; ++i) {
+            const int task = tid + i * DTHREADS;
+            const int kq = task % (DT / 4);
+            const int dq = task / (DT / 4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t key = k0 + 4 * kq + r;
+                vreg[i][r] = key < key_end
+                    ? *reinterpret_cast<const u32x4*>(vbase + key * kstep + dq * 8)
+                    : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int i = 0; i < K_CHUNKS; ++i) {
+            const int cidx = tid + i * DTHREADS;
+            const int row = cidx / CPR;
+            const int col = cidx % CPR;
+            *reinterpret_cast<u32x4*>(ks + row * KP + col * 8) = kreg[i];
+        }
+#pragma unroll
+        for (int i = 0; i < V_PER; ++i) {
+            const int task = tid + i * DTHREADS;
+            const int kq = task % (DT / 4);
+            const int dq = task / (DT / 4);
+            const int pos = vt_pos(kq);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int w = j >> 1;
+                const int sh = (j & 1) * 16;
+                const uint32_t e0 = (vreg[i][0][w] >> sh) & 0xffffu;
+                const uint32_t e1 = (vreg[i][1][w] >> sh) & 0xffffu;
+                const uint32_t e2 = (vreg[i][2][w] >> sh) & 0xffffu;
+                const uint32_t e3 = (vreg[i][3][w] >> sh) & 0xffffu;
+                u32x2 pk = {e0 | (e1 << 16), e2 | (e3 << 16)};
+                *reinterpret_cast<u32x2*>(vt + (dq * 8 + j) * DVP + pos) = pk;
+            }
+        }
+    };
+
+    load_tile(0);
+    for (int t = 0; t < n_tiles; ++t) {
+        store_tile();
+        __syncthreads();
+        if (t + 1 < n_tiles) load_tile(t + 1);
+
+        const uint32_t wk0 = key0 + (uint32_t)t * DT + wave * 32;   // this wave's first key
+        if (wk0 < key_end) {
+            f32x16 sacc[NQB];
+            const uint16_t* krow = ks + (wave * 32 + l32) * KP + hh * 8;
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) sacc[qb] = f32x16{};
+#pragma unroll
+            for (int e = 0; e < DSTEPS; ++e) {
+                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + 16 * e);
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb)
+                    sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][e], sacc[qb], 0, 0, 0);
+            }
+
+            bf16x8 pf[NQB][2];
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) {
+                // keys past the view end or after the query (mixing, new token) -> -inf
+                if (wk0 + 31 > qidx[qb] || wk0 + 31 >= key_end) {
+#pragma unroll
+                    for (int it = 0; it < 16; ++it) {
+                        const uint32_t key = wk0 + 8 * (it >> 2) + 4 * hh + (it & 3);
+                        if (key > qidx[qb] || key >= key_end) sacc[qb][it] = -INFINITY;
+                    }
+                }
+                float mx = -INFINITY;
+#pragma unroll
+                for (int it = 0; it < 16; ++it) mx = fmaxf(mx, sacc[qb][it]);
+                mx = fmaxf(mx, xor32(mx));
+                const float m_new = fmaxf(m_run[qb], mx * a.c);
+                const float m_use = m_new == -INFINITY ? 0.f : m_new;
+                const float alpha = fast_exp2(m_run[qb] - m_use);
+                m_run[qb] = m_new;
+                float rs = 0.f;
+#pragma unroll
+                for (int it = 0; it < 16; ++it) {
+                    const float p = fast_exp2(__builtin_fmaf(sacc[qb][it], a.c, -m_use));
+                    sacc[qb][it] = p;
+                    rs += p;
+                }
+                rs += xor32(rs);
+                l_run[qb] = l_run[qb] * alpha + rs;
+#pragma unroll
+                for (int i = 0; i < DBLK; ++i) oacc[qb][i] *= alpha;
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const int o8 = c * 8;
+                    u32x4 w;
+                    w[0] = pack_bf16x2(sacc[qb][o8 + 0], sacc[qb][o8 + 1]);
+                    w[1] = pack_bf16x2(sacc[qb][o8 + 2], sacc[qb][o8 + 3]);
+                    w[2] = pack_bf16x2(sacc[qb][o8 + 4], sacc[qb][o8 + 5]);
+                    w[3] = pack_bf16x2(sacc[qb][o8 + 6], sacc[qb][o8 + 7]);
+                    pf[qb][c] = __builtin_bit_cast(bf16x8, w);
+                }
+            }
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db) {
+                const uint16_t* vrow = vt + (db * 32 + l32) * DVP + wave * 32 + hh * 8;
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vrow + 16 * c);
+#pragma unroll
+                    for (int qb = 0; qb < NQB; ++qb)
+                        oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][c], oacc[qb][db], 0, 0, 0);
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- merge the 4 waves' partial softmax states through LDS ----
+    float* mo = reinterpret_cast<float*>(smem_raw);          // [wave][row][d]
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        const int row = qb * 32 + l32;
+        if (hh == 0) {
+            sm_m[wave][row] = m_run[qb];
+            sm_l[wave][row] = l_run[qb];
+        }
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+            for (int it = 0; it < 16; ++it) {
+                const int d = db * 32 + 8 * (it >> 2) + 4 * hh + (it & 3);
+                mo[(wave * NQB * 32 + row) * D + d] = oacc[qb][db][it];
+            }
+    }
+    __syncthreads();
+
+    const uint32_t r_base = a.within ? view * a.G : 0u;
+    for (int idx = tid; idx < (int)rows * D; idx += DTHREADS) {
+        const int row = idx / D;
+        const int d = idx - row * D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < DNW; ++w) M = fmaxf(M, sm_m[w][row]);
+        const float Mu = M == -INFINITY ? 0.f : M;
+        float o = 0.f, l = 0.f;
+#pragma unroll
+        for (int w = 0; w < DNW; ++w) {
+            const float f = fast_exp2(sm_m[w][row] - Mu);
+            o += f * mo[(w * NQB * 32 + row) * D + d];
+            l += f * sm_l[w][row];
+        }
+        const uint32_t r = r_base + row;
+        float* part = a.ws + ((((uint64_t)seq * a.Hkv + kvh) * a.R + r) * a.nsplit + sp) * (D + 2);
+        if (d == 0) {
+            part[0] = M;
+            part[1] = l;
+        }
+        part[2 + d] = o;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 3. combine
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256)
+decode_combine_kernel(const float* __restrict__ ws, const int32_t* __restrict__ tokens_before,
+                      uint16_t* __restrict__ out, uint32_t S, uint32_t n, uint32_t Hq,
+                      uint32_t Hkv, uint32_t G, uint32_t R, uint32_t nsplit, uint32_t split,
+                      uint32_t within, uint32_t max_tokens) {
+    const uint32_t idx = blockIdx.x * 256 + threadIdx.x;    // over S*Hkv*R*D
+    if (idx >= S * Hkv * R * D) return;
+    const uint32_t d = idx % D;
+    const uint32_t unit = idx / D;                             // (seq*Hkv + kvh)*R + r
+    const uint32_t r = unit % R;
+    const uint32_t sk = unit / R;
+    const uint32_t kvh = sk % Hkv;
+    const uint32_t seq = sk / Hkv;
+    const uint32_t T = clamp_tokens(tokens_before[seq], max_tokens);
+    const uint32_t len = within ? T + 1 : (T + 1) * n;
+    const uint32_t nvalid = (len + split - 1) / split;
+    const float* part = ws + (uint64_t)unit * nsplit * (D + 2);
+    float M = -INFINITY;
+    for (uint32_t sp = 0; sp < nvalid; ++sp) M = fmaxf(M, part[sp * (D + 2)]);
+    float o = 0.f, l = 0.f;
+    for (uint32_t sp = 0; sp < nvalid; ++sp) {
+        const float* p = part + sp * (D + 2);
+        const float f = fast_exp2(p[0] - M);
+        l += f * p[1];
+        o += f * p[2 + d];
+    }
+    const uint32_t s = r / G;
+    const uint32_t gh = r - s * G;
+    __bf16 hv = (__bf16)(o / l);
+    out[(((uint64_t)seq * n + s) * Hq + kvh * G + gh) * D + d] = __builtin_bit_cast(uint16_t, hv);
+}
+
+struct SplitPlan {
+    uint32_t nsplit, split;
+};
+
+SplitPlan plan_splits(uint64_t S, uint32_t n, uint32_t Hkv, uint64_t max_tokens, bool within) {
+    const uint64_t len_max = within ? max_tokens + 1 : (max_tokens + 1) * n;
+    const uint64_t units = S * Hkv * (within ? n : 1u);
+    uint64_t want = (kTargetBlocks + units - 1) / units;
+    const uint64_t max_splits = (len_max + DT - 1) / DT;
+    if (want > max_splits) want = max_splits;
+    if (want < 1) want = 1;
+    uint64_t split = (len_max + want - 1) / want;
+    split = (split + DT - 1) / DT * DT;
+    const uint64_t nsplit = (len_max + split - 1) / split;
+    return {(uint32_t)nsplit, (uint32_t)split};
+}
+
+bool decode_sizes_ok(int64_t S, int32_t n, int32_t Hq, int32_t Hkv, int32_t D,
+                     int64_t max_tokens) {
+    if (S < 0 || n < 1 || Hq < 1 || Hkv < 1 || max_tokens < 0) return false;
+    if (Hq % Hkv != 0) return false;
+    if (D != 64 && D != 128) return false;
+    if ((int64_t)n * (Hq / Hkv) > 64) return false;
+    if ((max_tokens + 1) * (int64_t)n > 0x7fffffffLL) return false;
+    if (S > 65535) return false;
+    return true;
+}
+
+}  // namespace
+
+}  // namespace hdsfa
+
+extern "C" size_t sfa_decode_workspace_size(int64_t S, int32_t n, int32_t Hq, int32_t Hkv,
+                                            int32_t D, int64_t max_tokens) {
+    using namespace hdsfa;
+    if (!decode_sizes_ok(S, n, Hq, Hkv, D, max_tokens)) return 0;
+    const SplitPlan pw = plan_splits((uint64_t)S, (uint32_t)n, (uint32_t)Hkv, (uint64_t)max_tokens, true);
+    const SplitPlan pm = plan_splits((uint64_t)S, (uint32_t)n, (uint32_t)Hkv, (uint64_t)max_tokens, false);
+    const uint64_t nsplit = pw.nsplit > pm.nsplit ? pw.nsplit : pm.nsplit;
+    const uint64_t R = (uint64_t)n * (Hq / Hkv);
+    return (size_t)((uint64_t)S * Hkv * R * nsplit * (uint64_t)(D + 2) * sizeof(float));
+}
+
+extern "C" hd_status sfa_decode_step(const uint16_t* q_new, const uint16_t* k_new,
+                                     const uint16_t* v_new, uint16_t* k_cache,
+                                     uint16_t* v_cache, const int32_t* tokens_before,
+                                     int64_t S, int32_t n, int32_t Hq, int32_t Hkv,
+                                     int32_t D, int64_t C_max, int64_t max_tokens,
+                                     int32_t mode, float softmax_scale, void* workspace,
+                                     size_t workspace_bytes, uint16_t* out,
+                                     hipStream_t stream) {
+    using namespace hdsfa;
+    if (S < 0 || n < 1 || Hq < 1 || Hkv < 1 || max_tokens < 0 || C_max < 0) return HD_ERR_SHAPE;
+    if (Hq % Hkv != 0) return HD_ERR_SHAPE;
+    if (mode != 0 && mode != 1) return HD_ERR_SHAPE;
+    if (!decode_sizes_ok(S, n, Hq, Hkv, D, max_tokens)) return HD_ERR_UNSUPPORTED;
+    if ((max_tokens + 1) * (int64_t)n > C_max) return HD_ERR_CAPACITY;
+    if (S == 0) return HD_OK;
+    if (q_new == nullptr || k_new == nullptr || v_new == nullptr || k_cache == nullptr ||
+        v_cache == nullptr || tokens_before == nullptr || out == nullptr)
+        return HD_ERR_NULL;
+    if (!aligned16(q_new) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+        !aligned16(v_cache) || !aligned16(out))
+        return HD_ERR_SHAPE;
+    const size_t need = sfa_decode_workspace_size(S, n, Hq, Hkv, D, max_tokens);
+    if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return HD_ERR_WORKSPACE;
+
+    const bool within = mode == 0;
+    const uint32_t G = (uint32_t)(Hq / Hkv);
+    const uint32_t R = (uint32_t)n * G;
+    const uint64_t cache_seq = (uint64_t)C_max * Hkv * D;
+
+    // 1. append
+    {
+        const uint32_t row_chunks = (uint32_t)Hkv * D / 8;
+        const uint64_t total = (uint64_t)S * n * row_chunks;
+        if (total > 0x7fffffffULL) return HD_ERR_UNSUPPORTED;
+        const uint32_t blocks = (uint32_t)((total + 255) / 256);
+        decode_append_kernel<<<dim3(blocks), dim3(256), 0, stream>>>(
+            reinterpret_cast<const u32x4*>(k_new), reinterpret_cast<const u32x4*>(v_new),
+            reinterpret_cast<u32x4*>(k_cache), reinterpret_cast<u32x4*>(v_cache),
+            tokens_before, (uint32_t)S, (uint32_t)n, row_chunks, cache_seq / 8,
+            (uint32_t)max_tokens);
+        const hd_status st = launch_status();
+        if (st != HD_OK) return st;
+    }
+
+    // 2. attend
+    const SplitPlan plan = plan_splits((uint64_t)S, (uint32_t)n, (uint32_t)Hkv, (uint64_t)max_tokens, within);
+    // the workspace stride uses the larger plan of the two modes
+    const SplitPlan pw = plan_splits((uint64_t)S, (uint32_t)n, (uint32_t)Hkv, (uint64_t)max_tokens, true);
+    const SplitPlan pm = plan_splits((uint64_t)S, (uint32_t)n, (uint32_t)Hkv, (uint64_t)max_tokens, false);
+    const uint32_t ws_nsplit = pw.nsplit > pm.nsplit ? pw.nsplit : pm.nsplit;
+
+    DecodeArgs a;
+    a.q = q_new;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    a.tokens_before = tokens_before;
+    a.ws = static_cast<float*>(workspace);
+    a.cache_seq = cache_seq;
+    a.n = (uint32_t)n;
+    a.Hq = (uint32_t)Hq;
+    a.Hkv = (uint32_t)Hkv;
+    a.G = G;
+    a.R = R;
+    a.max_tokens = (uint32_t)max_tokens;
+    a.nsplit = ws_nsplit;
+    a.split = plan.split;
+    a.within = within ? 1u : 0u;
+    a.c = softmax_scale * kLog2e;
+    const uint32_t rows = within ? G : R;
+    const dim3 grid(plan.nsplit, (uint32_t)Hkv * (within ? (uint32_t)n : 1u), (uint32_t)S);
+    if (D == 128) {
+        if (rows <= 32) decode_attend_kernel<128, 1><<<grid, dim3(DTHREADS), 0, stream>>>(a);
+        else            decode_attend_kernel<128, 2><<<grid, dim3(DTHREADS), 0, stream>>>(a);
+    } else {
+        if (rows <= 32) decode_attend_kernel<64, 1><<<grid, dim3(DTHREADS), 0, stream>>>(a);
+        else            decode_attend_kernel<64, 2><<<grid, dim3(DTHREADS), 0, stream>>>(a);
+    }
+    hd_status st = launch_status();
+    if (st != HD_OK) return st;
+
+    // 3. combine
+    const uint64_t total = (uint64_t)S * Hkv * R * D;
+    if (total > 0x7fffffffULL) return HD_ERR_UNSUPPORTED;
+    const uint32_t blocks = (uint32_t)((total + 255) / 256);
+    if (D == 128)
+        decode_combine_kernel<128><<<dim3(blocks), dim3(256), 0, stream>>>(
+            a.ws, tokens_before, out, (uint32_t)S, (uint32_t)n, (uint32_t)Hq, (uint32_t)Hkv, G, R,
+            ws_nsplit, plan.split, a.within, (uint32_t)max_tokens);
+    else
+        decode_combine_kernel<64><<<dim3(blocks), dim3(256), 0, stream>>>(
+            a.ws, tokens_before, out, (uint32_t)S, (uint32_t)n, (uint32_t)Hq, (uint32_t)Hkv, G, R,
+            ws_nsplit, plan.split, a.within, (uint32_t)max_tokens);
+    return launch_status();
+}

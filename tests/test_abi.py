@@ -1,0 +1,131 @@
+"""C-ABI library checks that need no GPU: it loads, exports every symbol the
+header declares, and rejects invalid arguments on the host before launching
+anything (these paths return before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sequence_length_latent_amd as hd
+from sequence_length_latent_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hd_sfa.h")
+
+OK, NULL, SHAPE, UNSUP, CAP, LAUNCH, WS = range(7)
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hd_\w+|sfa_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return hd.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert set(names) == {"hd_status_string", "hd_abi_version", "hd_expand", "sfa_stream_attn",
+                          "sfa_mix_attn", "sfa_decode_workspace_size", "sfa_decode_step"}
+    for name in names:
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, name
+
+
+def test_status_strings(lib):
+    assert lib.hd_abi_version() == 1
+    seen = set()
+    for code in range(7):
+        s = lib.hd_status_string(code).decode()
+        assert s and s not in seen
+        seen.add(s)
+    assert lib.hd_status_string(99).decode() == "unknown status"
+    assert lib.hd_status_string(-1).decode() == "unknown status"
+
+
+FAKE = 0x10000  # 16-byte aligned non-null host value; never dereferenced on error paths
+
+
+def test_expand_validation(lib):
+    assert lib.hd_expand(None, 1, 4, FAKE, 2, 10, 8, FAKE, None, None) == NULL
+    assert lib.hd_expand(FAKE, 1, 4, FAKE, 2, 10, 12, FAKE, None, None) == SHAPE   # H % 8
+    assert lib.hd_expand(FAKE, 1, 4, FAKE + 2, 2, 10, 8, FAKE, None, None) == SHAPE  # align
+    assert lib.hd_expand(FAKE, 1, 4, FAKE, 0, 10, 8, FAKE, None, None) == SHAPE    # n = 0
+    assert lib.hd_expand(FAKE, -1, 4, FAKE, 2, 10, 8, FAKE, None, None) == SHAPE
+    # zero work: OK without touching anything, even with NULL buffers
+    assert lib.hd_expand(None, 0, 4, None, 2, 10, 8, None, None, None) == OK
+    assert lib.hd_expand(None, 3, 0, None, 2, 10, 8, None, None, None) == OK
+
+
+@pytest.mark.parametrize("fn", ["sfa_stream_attn", "sfa_mix_attn"])
+def test_prefill_validation(lib, fn):
+    f = getattr(lib, fn)
+    assert f(None, FAKE, FAKE, FAKE, 1, 2, 8, 4, 2, 128, 1.0, None) == NULL
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 2, 8, 4, 3, 128, 1.0, None) == SHAPE     # Hq % Hkv
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 2, 8, 4, 2, 96, 1.0, None) == UNSUP      # D
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 0, 8, 4, 2, 128, 1.0, None) == SHAPE     # n
+    assert f(FAKE, FAKE + 8, FAKE, FAKE, 1, 2, 8, 4, 2, 128, 1.0, None) == SHAPE  # align
+    assert f(None, None, None, None, 0, 2, 8, 4, 2, 128, 1.0, None) == OK
+    assert f(None, None, None, None, 2, 2, 0, 4, 2, 128, 1.0, None) == OK
+
+
+def test_decode_workspace_size(lib):
+    # n4 decode workload: 64 sequences, 4096 cached tokens, 32/8 heads, D=128
+    size = lib.sfa_decode_workspace_size(64, 4, 32, 8, 128, 4096)
+    rows = 4 * (32 // 8)
+    per = 64 * 8 * rows * (128 + 2) * 4
+    assert size > 0 and size % per == 0
+    assert lib.sfa_decode_workspace_size(64, 4, 32, 8, 96, 4096) == 0       # D
+    assert lib.sfa_decode_workspace_size(64, 4, 32, 7, 128, 4096) == 0      # Hq % Hkv
+    assert lib.sfa_decode_workspace_size(64, 8, 128, 8, 128, 4096) == 0     # rows > 64
+
+
+def test_decode_validation(lib):
+    args = dict(S=2, n=4, Hq=8, Hkv=2, D=128, C=4 * 11, maxT=10, mode=1)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        ws = kw.get("ws", FAKE)
+        wsb = kw.get("wsb", 1 << 30)
+        return lib.sfa_decode_step(kw.get("q", FAKE), FAKE, FAKE, FAKE, FAKE, FAKE, a["S"], a["n"],
+                                   a["Hq"], a["Hkv"], a["D"], a["C"], a["maxT"], a["mode"], 0.1,
+                                   ws, wsb, FAKE, None)
+
+    assert call(q=None) == NULL
+    assert call(C=4 * 11 - 1) == CAP
+    assert call(mode=2) == SHAPE
+    assert call(Hkv=3) == SHAPE
+    assert call(D=80) == UNSUP
+    assert call(ws=None) == WS
+    assert call(wsb=16) == WS
+    assert call(S=0, q=None) == OK
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    q = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        hd.stream_attn(q, q, q, 2, 1.0)
+    with pytest.raises(ValueError):
+        hd.expand(torch.zeros(1, 2, dtype=torch.int32), torch.zeros(2, 5, 8, dtype=torch.bfloat16))
+
+
+def test_library_is_gfx950_only():
+    """The shared object carries only gfx950 device code."""
+    data = open(_lib.LIB_PATH, "rb").read()
+    assert b"gfx950" in data
+    for other in (b"gfx942", b"gfx90a", b"gfx1100", b"sm_"):
+        assert other + b"\x00" not in data and b"amdgcn-amd-amdhsa--" + other not in data
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "sequence_length_latent_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f

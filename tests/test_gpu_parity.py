@@ -1,0 +1,332 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every case draws seeded synthetic inputs (``sfa_inputs``), runs the library on
+the GPU, and compares with ``oracle`` on the very same bf16 bits: bit-exact for
+the expansion and the cache append, the floating-point bar of ``_check`` for
+attention.  Full-size workloads are checked on sampled rows that the oracle
+computes one by one, in the launch configuration the bench uses.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sequence_length_latent_amd as hd
+import sfa_inputs as si
+from tests._check import assert_close, close_report
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+WITHIN, MIX = oracle.WITHIN, oracle.MIX
+FNS = {WITHIN: hd.stream_attn, MIX: hd.mix_attn}
+
+
+def f64(t):
+    return oracle.bf16_bits_to_f64(si.bits(t))
+
+
+def _rand(shape, std, seed, device=DEV):
+    return si.randn_bf16(shape, std, seed, device)
+
+
+# ---------------------------------------------------------------------------
+# expansion (bit-exact)
+# ---------------------------------------------------------------------------
+def test_expand_tiny_bit_exact():
+    ids, tab = si.expand_inputs(si.TINY)
+    out = hd.expand(ids.to(DEV), tab.to(DEV))
+    ref, bad = oracle.expand_ref(ids.numpy(), si.bits(tab))
+    assert not bad
+    assert np.array_equal(si.bits(out), ref)
+
+
+@pytest.mark.parametrize("n,B,L,V,H", [(1, 1, 1, 7, 8), (3, 2, 33, 50, 24), (8, 1, 100, 300, 64),
+                                       (5, 3, 17, 1000, 4096), (2, 1, 1024, 64, 136)])
+def test_expand_shapes_bit_exact(n, B, L, V, H):
+    seed = 1000 + n * 7 + L
+    tab = _rand((n, V, H), 0.02, seed, "cpu")
+    g = torch.Generator().manual_seed(seed)
+    ids = torch.randint(0, V, (B, L), generator=g, dtype=torch.int64).to(torch.int32)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = hd.expand(ids.to(DEV), tab.to(DEV), err_flag=flag)
+    ref, bad = oracle.expand_ref(ids.numpy(), si.bits(tab))
+    assert np.array_equal(si.bits(out), ref)
+    assert int(flag.item()) == 0 and not bad
+
+
+def test_expand_out_of_range_ids():
+    n, V, H = 3, 20, 16
+    tab = _rand((n, V, H), 1.0, 77, "cpu")
+    ids = torch.tensor([[0, 20, 5, -3, 19]], dtype=torch.int32)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = hd.expand(ids.to(DEV), tab.to(DEV), err_flag=flag)
+    ref, bad = oracle.expand_ref(ids.numpy(), si.bits(tab))
+    assert bad and int(flag.item()) == 1
+    assert np.array_equal(si.bits(out), ref)
+
+
+def test_expand_n4_full_size_sampled():
+    """n=4 workload at full size: vocab 151936, hidden 4096 (4.98 GB of tables)."""
+    cfg = si.N4
+    ids, tab = si.expand_inputs(cfg, device=DEV)
+    out = hd.expand(ids, tab)
+    torch.cuda.synchronize()
+    g = torch.Generator().manual_seed(5)
+    tsel = torch.cat([torch.tensor([0, 1, cfg.L - 1]),
+                      torch.randint(0, cfg.L, (61,), generator=g)]).unique()
+    ids_h = ids.cpu()
+    # oracle over the sampled tokens, reading only the table rows they use
+    used = ids_h[:, tsel].unique()
+    sub_tab = si.bits(tab[:, used.to(DEV)])
+    remap = {int(t): i for i, t in enumerate(used)}
+    sub_ids = np.vectorize(lambda x: remap[int(x)])(ids_h[:, tsel].numpy())
+    ref, bad = oracle.expand_ref(sub_ids, sub_tab)
+    assert not bad
+    pos = (tsel[:, None] * cfg.n + torch.arange(cfg.n)[None, :]).reshape(-1)
+    got = si.bits(out[:, pos.to(DEV)])
+    assert np.array_equal(got, ref)
+    # and the whole output once, against a second gather route on the GPU
+    want = tab[torch.arange(cfg.n, device=DEV)[None, None, :], ids.long()[:, :, None]]
+    assert torch.equal(out.view(torch.int16), want.reshape(cfg.B, cfg.N, cfg.hidden).view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# prefill attention
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", [WITHIN, MIX])
+def test_prefill_tiny_all_rows(mode):
+    cfg = si.TINY
+    q, k, v = si.prefill_qkv(cfg)
+    out = FNS[mode](q.to(DEV), k.to(DEV), v.to(DEV), cfg.n, cfg.scale)
+    ref = oracle.prefill_ref(si.bits(q), si.bits(k), si.bits(v), cfg.n, mode, cfg.scale)
+    assert_close(f64(out), ref, f"tiny mode={mode}")
+
+
+SWEEP = [
+    # n, B, L, Hq, Hkv, D
+    (1, 1, 1, 1, 1, 64),
+    (1, 2, 65, 4, 2, 128),
+    (2, 1, 7, 8, 1, 128),
+    (3, 1, 64, 4, 2, 64),
+    (5, 1, 65, 8, 2, 128),
+    (8, 1, 100, 4, 4, 128),
+    (2, 2, 257, 8, 8, 64),
+    (4, 1, 129, 32, 8, 128),
+    (3, 1, 96, 16, 1, 128),
+    (8, 1, 33, 2, 2, 64),
+]
+
+
+@pytest.mark.parametrize("n,B,L,Hq,Hkv,D", SWEEP)
+@pytest.mark.parametrize("mode", [WITHIN, MIX])
+def test_prefill_sweep(n, B, L, Hq, Hkv, D, mode):
+    seed = 2000 + 97 * n + 13 * L + Hq + D
+    N = n * L
+    q = _rand((B, N, Hq, D), D ** -0.5, seed, "cpu")
+    k = _rand((B, N, Hkv, D), 1.0, seed + 1, "cpu")
+    v = _rand((B, N, Hkv, D), 1.0, seed + 2, "cpu")
+    out = FNS[mode](q.to(DEV), k.to(DEV), v.to(DEV), n, 1.0)
+    ref = oracle.prefill_ref(si.bits(q), si.bits(k), si.bits(v), n, mode, 1.0)
+    assert_close(f64(out), ref, f"sweep n={n} L={L} H={Hq}/{Hkv} D={D} mode={mode}")
+
+
+def _sample_rows(N, n, count, seed):
+    g = np.random.default_rng(seed)
+    fixed = [0, 1, n - 1, n, 31, 32, 63, 64, 127, 128, N // 2, N - n - 1, N - 2, N - 1]
+    rows = np.unique(np.concatenate([np.array([r for r in fixed if 0 <= r < N]),
+                                     g.integers(0, N, count)]))
+    return rows
+
+
+FULL = [
+    (si.N4, 0, WITHIN), (si.N4, 0, MIX),
+    (si.N8STACK, 0, WITHIN), (si.N8STACK, 3, MIX),
+    (si.LONG, 0, WITHIN), (si.LONG, 0, MIX),
+]
+
+
+@pytest.mark.parametrize("cfg,layer,mode", FULL, ids=lambda x: getattr(x, "name", str(x)))
+def test_prefill_full_size_sampled(cfg, layer, mode):
+    q, k, v = si.prefill_qkv(cfg, layer=layer, device=DEV)
+    out = FNS[mode](q, k, v, cfg.n, cfg.scale)
+    torch.cuda.synchronize()
+    rows = _sample_rows(cfg.N, cfg.n, 40, 11 + layer)
+    G = cfg.Hq // cfg.Hkv
+    heads = sorted({0, G - 1, G, cfg.Hq - 1})
+    for b in range(cfg.B):
+        ref = oracle.prefill_ref(si.bits(q[b:b + 1]), si.bits(k[b:b + 1]), si.bits(v[b:b + 1]),
+                                 cfg.n, mode, cfg.scale, rows=rows, heads=heads)
+        got = f64(out[b:b + 1][:, torch.as_tensor(rows, device=DEV)][:, :, heads])
+        assert_close(got, ref, f"{cfg.name} b={b} mode={mode}")
+
+
+def test_prefill_literal_scaling_reading():
+    """Second reading of 'Q/K/V ~N(0,1) pre-scaled by 1/sqrt(128)': all three scaled."""
+    cfg = si.N4
+    s = 128 ** -0.5
+    q, k, v = si.prefill_qkv(cfg, device=DEV, q_std=s, kv_std=s, B=1, L=256)
+    for mode in (WITHIN, MIX):
+        out = FNS[mode](q, k, v, cfg.n, 1.0)
+        ref = oracle.prefill_ref(si.bits(q), si.bits(k), si.bits(v), cfg.n, mode, 1.0,
+                                 heads=[0, 5, 31])
+        assert_close(f64(out[:, :, [0, 5, 31]]), ref, f"literal scaling mode={mode}")
+
+
+@pytest.mark.parametrize("mode", [WITHIN, MIX])
+def test_prefill_peaked_softmax(mode):
+    """Q ~ N(0,1) with scale 1: logits of std ~ sqrt(D), exercising the max rescale."""
+    n, L, Hq, Hkv, D = 4, 200, 8, 2, 128
+    q = _rand((1, n * L, Hq, D), 1.0, 31, "cpu")
+    k = _rand((1, n * L, Hkv, D), 1.0, 32, "cpu")
+    v = _rand((1, n * L, Hkv, D), 1.0, 33, "cpu")
+    out = FNS[mode](q.to(DEV), k.to(DEV), v.to(DEV), n, 1.0)
+    ref = oracle.prefill_ref(si.bits(q), si.bits(k), si.bits(v), n, mode, 1.0)
+    assert_close(f64(out), ref, "peaked")
+
+
+def test_prefill_exact_pins():
+    n, L, Hq, Hkv, D = 4, 70, 8, 2, 128
+    N = n * L
+    q = _rand((1, N, Hq, D), 1.0, 41)
+    k = _rand((1, N, Hkv, D), 1.0, 42)
+    v = _rand((1, N, Hkv, D), 1.0, 43)
+    vrep = v.repeat_interleave(Hq // Hkv, dim=2)
+    # L = 1 within-stream: every query sees only itself -> O == V bitwise
+    o1 = hd.stream_attn(q[:, :n].contiguous(), k[:, :n].contiguous(), v[:, :n].contiguous(), n, 1.0)
+    assert torch.equal(o1.view(torch.int16), vrep[:, :n].view(torch.int16))
+    # first token of every stream (within) and position 0 (mixing) -> O == V bitwise
+    ow = hd.stream_attn(q, k, v, n, 1.0)
+    om = hd.mix_attn(q, k, v, n, 1.0)
+    assert torch.equal(ow[:, :n].view(torch.int16), vrep[:, :n].view(torch.int16))
+    assert torch.equal(om[:, :1].view(torch.int16), vrep[:, :1].view(torch.int16))
+    # V == 1 -> O == 1 exactly (softmax rows sum to one)
+    ones = torch.ones_like(v)
+    for fn in (hd.stream_attn, hd.mix_attn):
+        o = fn(q, k, ones, n, 1.0)
+        assert torch.all(o == 1.0)
+
+
+def test_prefill_stream_one_hot_pin():
+    """V[p(t,s)] = e_s: within-stream output must be e_s for every query."""
+    n, L, Hq, Hkv, D = 5, 90, 4, 2, 64
+    N = n * L
+    q = _rand((1, N, Hq, D), 1.0, 51)
+    k = _rand((1, N, Hkv, D), 1.0, 52)
+    v = torch.zeros((1, N, Hkv, D), dtype=torch.bfloat16, device=DEV)
+    pos = torch.arange(N, device=DEV)
+    v[0, pos, :, pos % n] = 1.0
+    o = hd.stream_attn(q, k, v, n, 1.0)
+    want = torch.zeros((1, N, Hq, D), dtype=torch.float64, device=DEV)
+    want[0, pos, :, pos % n] = 1.0
+    assert_close(o.double().cpu().numpy(), want.cpu().numpy(), "one-hot")
+
+
+@pytest.mark.parametrize("mode", [WITHIN, MIX])
+def test_prefill_k_zero_prefix_means(mode):
+    n, L, Hq, Hkv, D = 3, 150, 4, 4, 128
+    N = n * L
+    q = _rand((1, N, Hq, D), 1.0, 61)
+    k = torch.zeros((1, N, Hkv, D), dtype=torch.bfloat16, device=DEV)
+    v = _rand((1, N, Hkv, D), 1.0, 62)
+    o = FNS[mode](q, k, v, n, 1.0)
+    vf = f64(v)[0]
+    if mode == MIX:
+        want = np.cumsum(vf, axis=0) / np.arange(1, N + 1)[:, None, None]
+    else:
+        want = np.empty_like(vf)
+        for s in range(n):
+            want[s::n] = np.cumsum(vf[s::n], axis=0) / np.arange(1, L + 1)[:, None, None]
+    assert_close(f64(o)[0], want, "prefix means")
+
+
+def test_negative_controls_fail_the_bar():
+    cfg = si.TINY
+    q, k, v = si.prefill_qkv(cfg, L=64)
+    q2 = _rand(q.shape, 1.0, 71, "cpu")   # peaked, so outputs are not all tiny
+    ref_w = oracle.prefill_ref(si.bits(q2), si.bits(k), si.bits(v), cfg.n, WITHIN, 1.0)
+    ref_m = oracle.prefill_ref(si.bits(q2), si.bits(k), si.bits(v), cfg.n, MIX, 1.0)
+    ow = f64(hd.stream_attn(q2.to(DEV), k.to(DEV), v.to(DEV), cfg.n, 1.0))
+    om = f64(hd.mix_attn(q2.to(DEV), k.to(DEV), v.to(DEV), cfg.n, 1.0))
+    assert close_report(ow, ref_w)[0] and close_report(om, ref_m)[0]
+    assert not close_report(np.zeros_like(ow), ref_w)[0]              # zero output
+    assert not close_report(np.roll(ow, 1, axis=1), ref_w)[0]         # rolled by one stream
+    assert not close_report(om, ref_w)[0]                             # mixing fed to within
+    assert not close_report(ow, ref_m)[0]
+
+
+def test_determinism():
+    cfg = si.N4
+    q, k, v = si.prefill_qkv(cfg, device=DEV, B=1, L=512)
+    for fn in (hd.stream_attn, hd.mix_attn):
+        a = fn(q, k, v, cfg.n, 1.0)
+        b = fn(q, k, v, cfg.n, 1.0)
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+def _decode_case(cfg, S, T, tb, mode, seqs=None, max_tokens=None, device=DEV):
+    qn, kn, vn, kc, vc, tbt = si.decode_inputs(cfg, device=device, S=S, T=T, tokens_before=tb)
+    max_tokens = T if max_tokens is None else max_tokens
+    kc0, vc0 = kc.clone(), vc.clone()
+    out = hd.decode_step(qn, kn, vn, kc, vc, tbt, cfg.n, max_tokens, mode, cfg.scale)
+    torch.cuda.synchronize()
+    seqs = list(range(S)) if seqs is None else seqs
+    tbh = tbt.cpu().numpy()
+    for qi in seqs:
+        sl = slice(qi, qi + 1)
+        k2, v2 = oracle.decode_append_ref(si.bits(kc0[sl]), si.bits(vc0[sl]), si.bits(kn[sl]),
+                                          si.bits(vn[sl]), tbh[sl], cfg.n)
+        assert np.array_equal(si.bits(kc[sl]), k2), f"k append seq {qi}"
+        assert np.array_equal(si.bits(vc[sl]), v2), f"v append seq {qi}"
+        ref = oracle.decode_ref(si.bits(qn[sl]), k2, v2, tbh[sl], cfg.n, mode, cfg.scale)
+        assert_close(f64(out[sl]), ref, f"decode seq {qi} T={tbh[qi]} mode={mode}")
+    return out
+
+
+@pytest.mark.parametrize("mode", [WITHIN, MIX])
+def test_decode_small_ragged(mode):
+    _decode_case(si.DECODE, S=5, T=300, tb=[300, 0, 1, 129, 255], mode=mode)
+
+
+@pytest.mark.parametrize("mode", [WITHIN, MIX])
+def test_decode_other_shapes(mode):
+    # n=3 (not a power of two), G=8 -> 24 rows; D=64
+    cfg = si.DecodeCfg("d3", 9, S=3, n=3, T=200, Hq=16, Hkv=2, D=64, scale=0.125)
+    _decode_case(cfg, S=3, T=200, tb=[200, 77, 3], mode=mode)
+    # n=8, G=8 -> 64 rows in mixing mode (two 32-row blocks)
+    cfg = si.DecodeCfg("d8", 10, S=2, n=8, T=70, Hq=8, Hkv=1, D=128, scale=0.09)
+    _decode_case(cfg, S=2, T=70, tb=[70, 31], mode=mode)
+
+
+@pytest.mark.parametrize("mode", [WITHIN, MIX])
+def test_decode_full_size_sampled(mode):
+    """Decode workload at full size: 64 sequences x 16384 cached entries."""
+    cfg = si.DECODE
+    _decode_case(cfg, S=cfg.S, T=cfg.T, tb=None, mode=mode, seqs=[0, 31, 63])
+
+
+def test_decode_idempotent_append_and_modes_share_cache():
+    cfg = si.DECODE
+    S, T = 4, 64
+    qn, kn, vn, kc, vc, tb = si.decode_inputs(cfg, device=DEV, S=S, T=T)
+    a = hd.decode_step(qn, kn, vn, kc, vc, tb, cfg.n, T, WITHIN, cfg.scale)
+    kc1 = kc.clone()
+    b = hd.decode_step(qn, kn, vn, kc, vc, tb, cfg.n, T, WITHIN, cfg.scale)
+    assert torch.equal(kc.view(torch.int16), kc1.view(torch.int16))
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("mode", [WITHIN, MIX])
+def test_decode_matches_prefill_tail_on_gpu(mode):
+    """Decode of token T equals the last n rows of a prefill over T+1 tokens."""
+    n, Hq, Hkv, D, T = 4, 32, 8, 128, 150
+    cfg = si.DecodeCfg("dp", 11, S=1, n=n, T=T, Hq=Hq, Hkv=Hkv, D=D, scale=D ** -0.5)
+    qn, kn, vn, kc, vc, tb = si.decode_inputs(cfg, device=DEV, S=1, T=T)
+    out = hd.decode_step(qn, kn, vn, kc, vc, tb, n, T, mode, cfg.scale)
+    N = (T + 1) * n
+    qp = _rand((1, N, Hq, D), 1.0, 81)
+    qp[0, T * n:] = qn[0]
+    pre = FNS[mode](qp, kc[:, :N].contiguous(), vc[:, :N].contiguous(), n, cfg.scale)
+    assert_close(f64(out[0]), f64(pre[0, T * n:]), "decode vs prefill tail")
