@@ -19,15 +19,20 @@ constexpr int kWave = 64;
 // log2(e): the softmax is evaluated as exp2(s * scale * log2(e) - m).
 constexpr float kLog2e = 1.4426950408889634f;
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
 // Round-to-nearest-even float -> bf16 pair packed in one 32-bit word
-// (lo in bits 0..15).  The compiler lowers the __bf16 conversion to the
-// hardware convert on gfx950.
+// (lo in bits 0..15): one v_cvt_pk_bf16_f32 on gfx950.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    __bf16 a = (__bf16)lo;
-    __bf16 b = (__bf16)hi;
-    uint16_t ua = __builtin_bit_cast(uint16_t, a);
-    uint16_t ub = __builtin_bit_cast(uint16_t, b);
-    return (uint32_t)ua | ((uint32_t)ub << 16);
+    const bf16x2 r = __builtin_convertvector(f32x2{lo, hi}, bf16x2);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// Eight floats -> eight bf16 (RNE) as one MFMA operand.
+__device__ __forceinline__ bf16x8 to_bf16x8(f32x8 x) {
+    return __builtin_convertvector(x, bf16x8);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) {

@@ -40,7 +40,6 @@ constexpr int BN = 64;       // keys per tile
 constexpr int MQ = 32;       // query rows per wave
 constexpr int NW = 4;        // waves per workgroup
 constexpr int THREADS = NW * kWave;
-constexpr int VP = BN + 8;   // transposed-V row pitch (elements)
 
 struct PrefillArgs {
     const uint16_t* q;
@@ -64,29 +63,56 @@ struct PrefillArgs {
     float c;             // softmax scale * log2(e)
 };
 
-// Position, within the transposed-V row, of the first of 4 consecutive keys
-// 4*kq .. 4*kq+3 (see the file comment).
-__device__ __forceinline__ int vt_pos(int kq) {
-    const int qq = kq & 3;
-    return 16 * (kq >> 2) + ((qq & 1) << 3) + ((qq >> 1) << 2);
+// XOR swizzle of the 16-byte chunks of a K/V row in LDS (rows of D bf16 =
+// D/8 chunks).  Consecutive rows permute their chunks so that both the 16-byte
+// K reads (32 rows, same logical chunk) and the 8-byte transpose reads of V
+// (4 consecutive rows x 2 chunks per 16 lanes) hit distinct banks.
+template <int D>
+__device__ __forceinline__ uint32_t swz(uint32_t row) {
+    constexpr uint32_t H = D / 16;            // half the chunks per row
+    return ((row & (H - 1)) << 1) | ((row / H) & 1u);
+}
+
+// Eight transpose reads of V for one 32-dim block: the two key quads (rd = 0,
+// 1) of each of the four 16-key steps c (immediate offsets c * 16 rows).  The
+// reads are issued from inline assembly so that the compiler does not order
+// them behind the asynchronous global->LDS loads of the next tile, which
+// target the other LDS stage; the block waits for its own results before it
+// returns, so every output register is complete when the asm ends.
+template <int ROWB>
+__device__ __forceinline__ void v_tr_reads(uint32_t a0, uint32_t a1, u32x2 (&r)[8]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %9\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:%10\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:%10\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:%11\n\t"
+        "ds_read_b64_tr_b16 %5, %9 offset:%11\n\t"
+        "ds_read_b64_tr_b16 %6, %8 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %7, %9 offset:%12\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]),
+          "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(a0), "v"(a1), "i"(16 * ROWB), "i"(32 * ROWB), "i"(48 * ROWB)
+        : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
 template <int D>
 __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 sfa_prefill_kernel(const PrefillArgs a) {
-    constexpr int KP = D + 8;                  // K row pitch (elements)
-    constexpr int KS_ELEMS = BN * KP;
-    constexpr int VT_ELEMS = D * VP;
-    constexpr int BUF_ELEMS = KS_ELEMS + VT_ELEMS;
+    constexpr int ROWB = D * 2;                // bytes per K/V row
+    constexpr int TILE_B = BN * ROWB;          // one K (or V) tile
+    constexpr int STAGE_B = 2 * TILE_B;        // K tile then V tile
+    constexpr int LOADS = TILE_B / (THREADS * 16);   // 16-byte direct loads per thread per tile
     constexpr int DSTEPS = D / 16;             // k-steps of the score product
     constexpr int DBLK = D / 32;               // 32-row blocks of O^T
-    constexpr int CPR = D / 8;                 // 16-byte chunks per row
-    constexpr int K_CHUNKS = BN * CPR / THREADS;        // per thread
-    constexpr int V_TASKS = (BN / 4) * (D / 8);         // (key quad, d octet)
-    static_assert(BN * CPR % THREADS == 0, "tile/thread mismatch");
-    static_assert(V_TASKS <= THREADS, "tile/thread mismatch");
+    static_assert(TILE_B % (THREADS * 16) == 0, "tile/thread mismatch");
 
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BUF_ELEMS];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE_B];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -113,8 +139,8 @@ sfa_prefill_kernel(const PrefillArgs a) {
 
     const uint16_t* qbase = a.q + b * a.q_batch + grp * a.q_group + (uint64_t)head * D;
     uint16_t* obase = a.o + b * a.q_batch + grp * a.q_group + (uint64_t)head * D;
-    const uint16_t* kbase = a.k + b * a.kv_batch + grp * a.kv_group + (uint64_t)kvh * D;
-    const uint16_t* vbase = a.v + b * a.kv_batch + grp * a.kv_group + (uint64_t)kvh * D;
+    const char* kview = reinterpret_cast<const char*>(a.k + b * a.kv_batch + grp * a.kv_group + (uint64_t)kvh * D);
+    const char* vview = reinterpret_cast<const char*>(a.v + b * a.kv_batch + grp * a.kv_group + (uint64_t)kvh * D);
 
     const uint32_t wg_end = min(a.len, (qtile + 1) * (uint32_t)BT);
     const int n_kt = (int)((wg_end + BN - 1) / BN);
@@ -140,81 +166,94 @@ sfa_prefill_kernel(const PrefillArgs a) {
     float m_run = -INFINITY;   // running max, in log2 units (already * c)
     float l_run = 0.f;         // running sum of exp2
 
-    // ---- K/V tile staging (global -> registers -> LDS) ----
-    u32x4 kreg[K_CHUNKS];
-    u32x4 vreg[4];
-    const int vkq = tid % (BN / 4);            // key quad of this thread's V task
-    const int vdo = tid / (BN / 4);            // d octet
-    const bool vtask = tid < V_TASKS;
-
-    auto load_tile = [&](int kt) {
+    // ---- direct global->LDS tile loads ----
+    // Load j of this wave fills LDS bytes [(wave*LOADS + j)*1024, +1024) of the
+    // tile, lane i its 16 bytes at +16*i: tile row r, physical chunk p, which
+    // holds logical chunk p ^ swz(r).  Rows past the view end (last tile only)
+    // are clamped to the last valid row: such keys lie in the future of every
+    // valid query, the causal mask gives them probability 0, and the finite
+    // values they hold never reach the output.
+    const uint32_t kv_row_b = (uint32_t)a.kv_row * 2u;
+    uint32_t ld_row[LOADS], ld_off[LOADS];
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+        const uint32_t lin = (uint32_t)(wave * LOADS + j) * 1024u + (uint32_t)lane * 16u;
+        const uint32_t row = lin / ROWB;
+        const uint32_t pch = (lin % ROWB) / 16u;
+        ld_row[j] = row;
+        ld_off[j] = row * kv_row_b + ((pch ^ swz<D>(row)) << 4);
+    }
+    auto issue_tile = [&](int kt, int stage) {
         const uint32_t k0 = (uint32_t)kt * BN;
+        const char* kt_base = kview + (uint64_t)k0 * kv_row_b;
+        const char* vt_base = vview + (uint64_t)k0 * kv_row_b;
+        unsigned char* ks = smem + stage * STAGE_B;
+        const bool full = k0 + BN <= a.len;
+        const uint32_t last = a.len - 1 - k0;
 #pragma unroll
-        for (int i = 0; i < K_CHUNKS; ++i) {
-            const int cidx = tid + i * THREADS;
-            const int row = cidx / CPR;
-            const int col = cidx % CPR;
-            const uint32_t key = k0 + row;
-            kreg[i] = key < a.len
-                ? *reinterpret_cast<const u32x4*>(kbase + (uint64_t)key * a.kv_row + col * 8)
-                : u32x4{0u, 0u, 0u, 0u};
-        }
-        if (vtask) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const uint32_t key = k0 + 4 * vkq + r;
-                vreg[r] = key < a.len
-                    ? *reinterpret_cast<const u32x4*>(vbase + (uint64_t)key * a.kv_row + vdo * 8)
-                    : u32x4{0u, 0u, 0u, 0u};
+        for (int j = 0; j < LOADS; ++j) {
+            uint32_t off = ld_off[j];
+            if (!full) {
+                const uint32_t rr = min(ld_row[j], last);
+                off -= (ld_row[j] - rr) * kv_row_b;
             }
-        }
-    };
-    auto store_tile = [&](int buf) {
-        uint16_t* ks = smem + buf * BUF_ELEMS;
-        uint16_t* vt = ks + KS_ELEMS;
-#pragma unroll
-        for (int i = 0; i < K_CHUNKS; ++i) {
-            const int cidx = tid + i * THREADS;
-            const int row = cidx / CPR;
-            const int col = cidx % CPR;
-            *reinterpret_cast<u32x4*>(ks + row * KP + col * 8) = kreg[i];
-        }
-        if (vtask) {
-            const int pos = vt_pos(vkq);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int w = j >> 1;
-                const int sh = (j & 1) * 16;
-                const uint32_t e0 = (vreg[0][w] >> sh) & 0xffffu;
-                const uint32_t e1 = (vreg[1][w] >> sh) & 0xffffu;
-                const uint32_t e2 = (vreg[2][w] >> sh) & 0xffffu;
-                const uint32_t e3 = (vreg[3][w] >> sh) & 0xffffu;
-                u32x2 pk = {e0 | (e1 << 16), e2 | (e3 << 16)};
-                *reinterpret_cast<u32x2*>(vt + (vdo * 8 + j) * VP + pos) = pk;
-            }
+            unsigned char* dst = ks + (wave * LOADS + j) * 1024;
+            __builtin_amdgcn_global_load_lds(
+                (const void __attribute__((address_space(1)))*)(kt_base + off),
+                (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(
+                (const void __attribute__((address_space(1)))*)(vt_base + off),
+                (void __attribute__((address_space(3)))*)(dst + TILE_B), 16, 0, 0);
         }
     };
 
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
+    // ---- per-lane LDS read offsets (independent of the tile) ----
+    // K (A operand of S^T = K Q^T): row kb*32 + l32, logical chunk 2e + hh.
+    const uint32_t kswz = swz<D>((uint32_t)l32);
+    uint32_t koff[DSTEPS];
+#pragma unroll
+    for (int e = 0; e < DSTEPS; ++e)
+        koff[e] = (uint32_t)l32 * ROWB + ((((uint32_t)(2 * e + hh)) ^ kswz) << 4);
+    // V (A operand of O^T = V^T P^T) through the transpose read: in each
+    // 16-lane group g, lane r = 4k + a addresses key row (16c + 4*(g/2) + k +
+    // 8*rd) at dims 32db + 16*(g%2) + 4a; lane i of the group then receives
+    // dim 32db + 16*(g%2) + i of those 4 keys, i.e. 4 of the 8 keys that the
+    // P^T operand holds in the same slots.
+    const uint32_t vg = (uint32_t)lane >> 4, vr = (uint32_t)lane & 15u;
+    const uint32_t vk = vr >> 2, va = vr & 3u;
+    uint32_t voff[2][DBLK];
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+        const uint32_t key = 4u * (vg >> 1) + vk + 8u * rd;
+        const uint32_t sw = swz<D>(key);
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+            const uint32_t lch = 4u * db + 2u * (vg & 1u) + (va >> 1);
+            voff[rd][db] = key * ROWB + ((lch ^ sw) << 4) + (va & 1u) * 8u;
+        }
+    }
+
+    issue_tile(0, 0);
 
     for (int kt = 0; kt < n_kt; ++kt) {
-        if (kt + 1 < n_kt) load_tile(kt + 1);
+        // this wave's loads of tile kt have landed; the barrier makes every
+        // wave's loads visible and frees the other stage for tile kt+1
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (kt + 1 < n_kt) issue_tile(kt + 1, (kt + 1) & 1);
 
         if (kt < wave_kt) {
-            const uint16_t* ks = smem + (kt & 1) * BUF_ELEMS;
-            const uint16_t* vt = ks + KS_ELEMS;
+            const unsigned char* ks = smem + (kt & 1) * STAGE_B;
+            const unsigned char* vs = ks + TILE_B;
 
             // S^T[key][query] for two 32-key blocks
             f32x16 sacc[BN / 32];
 #pragma unroll
             for (int kb = 0; kb < BN / 32; ++kb) {
                 sacc[kb] = f32x16{};
-                const uint16_t* krow = ks + (kb * 32 + l32) * KP + hh * 8;
 #pragma unroll
                 for (int e = 0; e < DSTEPS; ++e) {
-                    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + 16 * e);
+                    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + kb * 32 * ROWB + koff[e]);
                     sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[e], sacc[kb], 0, 0, 0);
                 }
             }
@@ -241,21 +280,27 @@ sfa_prefill_kernel(const PrefillArgs a) {
             const float m_new = fmaxf(m_run, mx * a.c);
             const float m_use = m_new == -INFINITY ? 0.f : m_new;
             const float alpha = fast_exp2(m_run - m_use);
+            // O only needs rescaling when some lane's running max moved
+            const bool moved = __builtin_amdgcn_ballot_w64(m_new > m_run) != 0;
             m_run = m_new;
 
-            float rs = 0.f;
+            // four independent partial sums keep the exp -> add chain short
+            float rsp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
                 for (int it = 0; it < 16; ++it) {
                     const float p = fast_exp2(__builtin_fmaf(sacc[kb][it], a.c, -m_use));
                     sacc[kb][it] = p;
-                    rs += p;
+                    rsp[it & 3] += p;
                 }
+            float rs = (rsp[0] + rsp[1]) + (rsp[2] + rsp[3]);
             rs += xor32(rs);
             l_run = l_run * alpha + rs;
+            if (moved) {
 #pragma unroll
-            for (int i = 0; i < DBLK; ++i) oacc[i] *= alpha;
+                for (int i = 0; i < DBLK; ++i) oacc[i] *= alpha;
+            }
 
             // P^T fragments (B operand): 16-key step c takes items 8*(c%2)..+7
             bf16x8 pf[BN / 16];
@@ -263,28 +308,25 @@ sfa_prefill_kernel(const PrefillArgs a) {
             for (int c = 0; c < BN / 16; ++c) {
                 const f32x16& s = sacc[c >> 1];
                 const int o8 = (c & 1) * 8;
-                u32x4 w;
-                w[0] = pack_bf16x2(s[o8 + 0], s[o8 + 1]);
-                w[1] = pack_bf16x2(s[o8 + 2], s[o8 + 3]);
-                w[2] = pack_bf16x2(s[o8 + 4], s[o8 + 5]);
-                w[3] = pack_bf16x2(s[o8 + 6], s[o8 + 7]);
-                pf[c] = __builtin_bit_cast(bf16x8, w);
+                pf[c] = to_bf16x8(f32x8{s[o8 + 0], s[o8 + 1], s[o8 + 2], s[o8 + 3],
+                                        s[o8 + 4], s[o8 + 5], s[o8 + 6], s[o8 + 7]});
             }
 
             // O^T[d][query] += V^T P^T
+            static_assert(BN == 64, "the transpose-read helper covers 4 steps of 16 keys");
+            const uint32_t vbase = lds_addr(vs);
 #pragma unroll
             for (int db = 0; db < DBLK; ++db) {
-                const uint16_t* vrow = vt + (db * 32 + l32) * VP + hh * 8;
+                u32x2 vr[8];
+                v_tr_reads<ROWB>(vbase + voff[0][db], vbase + voff[1][db], vr);
 #pragma unroll
                 for (int c = 0; c < BN / 16; ++c) {
-                    const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vrow + 16 * c);
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[c], oacc[db], 0, 0, 0);
+                    const u32x4 w = {vr[2 * c][0], vr[2 * c][1], vr[2 * c + 1][0], vr[2 * c + 1][1]};
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, w), pf[c], oacc[db], 0, 0, 0);
                 }
             }
         }
-
-        if (kt + 1 < n_kt) store_tile((kt + 1) & 1);
-        __syncthreads();
     }
 
     // ---- epilogue: O = O^T / l, lane writes 4 consecutive dims per item group ----
