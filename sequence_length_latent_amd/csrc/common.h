@@ -44,6 +44,20 @@ __device__ __forceinline__ float xor32(float x) {
     return __shfl_xor(x, 32, kWave);
 }
 
+// max / sum of x over lanes l and l^32, in registers (v_permlane32_swap):
+// swapping the upper half of one copy with the lower half of another leaves
+// lane l holding both x[l % 32] and x[l % 32 + 32].
+__device__ __forceinline__ float halves_max(float x) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
 inline bool aligned16(const void* p) {
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }

@@ -38,7 +38,8 @@ namespace {
 
 constexpr int BN = 64;       // keys per tile
 constexpr int MQ = 32;       // query rows per wave
-constexpr int NW = 4;        // waves per workgroup
+constexpr int NW = 8;        // waves per workgroup (2 per SIMD)
+constexpr int NSTAGE = 3;    // LDS ring depth for K and for V tiles
 constexpr int THREADS = NW * kWave;
 
 struct PrefillArgs {
@@ -57,20 +58,24 @@ struct PrefillArgs {
     uint32_t B;
     uint32_t Hkv;
     uint32_t G;          // query heads per KV head
-    uint32_t P;          // query heads packed per workgroup (1, 2 or 4)
+    uint32_t P;          // query heads packed per workgroup (1, 2, 4 or 8)
     uint32_t n_hpacks;   // G / P
     uint32_t n_qtiles;   // ceil(len / (MQ * NW / P))
     float c;             // softmax scale * log2(e)
 };
 
 // XOR swizzle of the 16-byte chunks of a K/V row in LDS (rows of D bf16 =
-// D/8 chunks).  Consecutive rows permute their chunks so that both the 16-byte
-// K reads (32 rows, same logical chunk) and the 8-byte transpose reads of V
-// (4 consecutive rows x 2 chunks per 16 lanes) hit distinct banks.
+// D/8 chunks).  Two read patterns must hit distinct banks:
+//   K:  16 consecutive rows, one logical chunk each (16-byte reads);
+//   V:  per 32 lanes, 4 consecutive rows x 4 consecutive logical chunks
+//       (8-byte transpose reads).
+// D=128 (256-byte rows span all 64 banks): swz = (r%4)*4 + (r/4)%4.
+// D=64 (128-byte rows, even/odd rows on opposite bank halves): the same idea
+// over rows of one parity: swz = ((r/2)%2)*4 + (r/4)%4.
 template <int D>
 __device__ __forceinline__ uint32_t swz(uint32_t row) {
-    constexpr uint32_t H = D / 16;            // half the chunks per row
-    return ((row & (H - 1)) << 1) | ((row / H) & 1u);
+    if constexpr (D == 128) return ((row & 3u) << 2) | ((row >> 2) & 3u);
+    else return (((row >> 1) & 1u) << 2) | ((row >> 2) & 3u);
 }
 
 // Eight transpose reads of V for one 32-dim block: the two key quads (rd = 0,
@@ -112,7 +117,7 @@ sfa_prefill_kernel(const PrefillArgs a) {
     constexpr int DBLK = D / 32;               // 32-row blocks of O^T
     static_assert(TILE_B % (THREADS * 16) == 0, "tile/thread mismatch");
 
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE_B];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * STAGE_B];   // K ring, V ring
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -167,7 +172,7 @@ sfa_prefill_kernel(const PrefillArgs a) {
     float l_run = 0.f;         // running sum of exp2
 
     // ---- direct global->LDS tile loads ----
-    // Load j of this wave fills LDS bytes [(wave*LOADS + j)*1024, +1024) of the
+    // Load j of this wave fills LDS bytes [(wave*LOADS + j)*1024, +1024) of a
     // tile, lane i its 16 bytes at +16*i: tile row r, physical chunk p, which
     // holds logical chunk p ^ swz(r).  Rows past the view end (last tile only)
     // are clamped to the last valid row: such keys lie in the future of every
@@ -183,27 +188,18 @@ sfa_prefill_kernel(const PrefillArgs a) {
         ld_row[j] = row;
         ld_off[j] = row * kv_row_b + ((pch ^ swz<D>(row)) << 4);
     }
-    auto issue_tile = [&](int kt, int stage) {
+    auto issue = [&](const char* view, int kt, unsigned char* buf) {
         const uint32_t k0 = (uint32_t)kt * BN;
-        const char* kt_base = kview + (uint64_t)k0 * kv_row_b;
-        const char* vt_base = vview + (uint64_t)k0 * kv_row_b;
-        unsigned char* ks = smem + stage * STAGE_B;
+        const char* base = view + (uint64_t)k0 * kv_row_b;
         const bool full = k0 + BN <= a.len;
         const uint32_t last = a.len - 1 - k0;
 #pragma unroll
         for (int j = 0; j < LOADS; ++j) {
             uint32_t off = ld_off[j];
-            if (!full) {
-                const uint32_t rr = min(ld_row[j], last);
-                off -= (ld_row[j] - rr) * kv_row_b;
-            }
-            unsigned char* dst = ks + (wave * LOADS + j) * 1024;
+            if (!full) off -= (ld_row[j] - min(ld_row[j], last)) * kv_row_b;
             __builtin_amdgcn_global_load_lds(
-                (const void __attribute__((address_space(1)))*)(kt_base + off),
-                (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(
-                (const void __attribute__((address_space(1)))*)(vt_base + off),
-                (void __attribute__((address_space(3)))*)(dst + TILE_B), 16, 0, 0);
+                (const void __attribute__((address_space(1)))*)(base + off),
+                (void __attribute__((address_space(3)))*)(buf + (wave * LOADS + j) * 1024), 16, 0, 0);
         }
     };
 
@@ -233,100 +229,149 @@ sfa_prefill_kernel(const PrefillArgs a) {
         }
     }
 
-    issue_tile(0, 0);
-
-    for (int kt = 0; kt < n_kt; ++kt) {
-        // this wave's loads of tile kt have landed; the barrier makes every
-        // wave's loads visible and frees the other stage for tile kt+1
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (kt + 1 < n_kt) issue_tile(kt + 1, (kt + 1) & 1);
-
-        if (kt < wave_kt) {
-            const unsigned char* ks = smem + (kt & 1) * STAGE_B;
-            const unsigned char* vs = ks + TILE_B;
-
-            // S^T[key][query] for two 32-key blocks
-            f32x16 sacc[BN / 32];
+    // S^T[key][query] = K Q^T for the two 32-key blocks of a tile
+    auto qk = [&](const unsigned char* ks, f32x16 (&sacc)[BN / 32]) {
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb) sacc[kb] = f32x16{};
+#pragma unroll
+        for (int e = 0; e < DSTEPS; ++e)
 #pragma unroll
             for (int kb = 0; kb < BN / 32; ++kb) {
-                sacc[kb] = f32x16{};
-#pragma unroll
-                for (int e = 0; e < DSTEPS; ++e) {
-                    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + kb * 32 * ROWB + koff[e]);
-                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[e], sacc[kb], 0, 0, 0);
-                }
+                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + kb * 32 * ROWB + koff[e]);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[e], sacc[kb], 0, 0, 0);
             }
+    };
 
-            // causal mask, only where the tile reaches past the wave's first query
+    // online softmax of one tile's scores; returns the P^T operands.  The
+    // causal mask is needed only on a wave's last (diagonal) tile.
+    auto softmax = [&](f32x16 (&sacc)[BN / 32], int kt, bool diag, bf16x8 (&pf)[BN / 16]) {
+        if (diag) {
             const uint32_t k0 = (uint32_t)kt * BN;
-            if (k0 + BN - 1 > q0) {
-#pragma unroll
-                for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-                    for (int it = 0; it < 16; ++it) {
-                        const uint32_t key = k0 + kb * 32 + 8 * (it >> 2) + 4 * hh + (it & 3);
-                        if (key > qi) sacc[kb][it] = -INFINITY;
-                    }
-            }
-
-            // online softmax (per lane = per query; halves exchange once)
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-                for (int it = 0; it < 16; ++it) mx = fmaxf(mx, sacc[kb][it]);
-            mx = fmaxf(mx, xor32(mx));
-            const float m_new = fmaxf(m_run, mx * a.c);
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = fast_exp2(m_run - m_use);
-            // O only needs rescaling when some lane's running max moved
-            const bool moved = __builtin_amdgcn_ballot_w64(m_new > m_run) != 0;
-            m_run = m_new;
-
-            // four independent partial sums keep the exp -> add chain short
-            float rsp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
                 for (int it = 0; it < 16; ++it) {
-                    const float p = fast_exp2(__builtin_fmaf(sacc[kb][it], a.c, -m_use));
-                    sacc[kb][it] = p;
-                    rsp[it & 3] += p;
+                    const uint32_t key = k0 + kb * 32 + 8 * (it >> 2) + 4 * hh + (it & 3);
+                    if (key > qi) sacc[kb][it] = -INFINITY;
                 }
-            float rs = (rsp[0] + rsp[1]) + (rsp[2] + rsp[3]);
-            rs += xor32(rs);
-            l_run = l_run * alpha + rs;
-            if (moved) {
+        }
+        float mx = -INFINITY;
 #pragma unroll
-                for (int i = 0; i < DBLK; ++i) oacc[i] *= alpha;
+        for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+            for (int it = 0; it < 16; ++it) mx = fmaxf(mx, sacc[kb][it]);
+        mx = halves_max(mx) * a.c;
+        // Lazy rescale: the reference max m_run only moves when a row's tile
+        // max exceeds it by more than 8 (a factor 2^8), so O and l are
+        // rescaled rarely (always on the first tile).  Probabilities stay
+        // <= 2^8 and the result O / l is unchanged.
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.f) != 0) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = fast_exp2(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < DBLK; ++i) oacc[i] *= alpha;
+        }
+        float rsp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+            for (int it = 0; it < 16; ++it) {
+                const float p = fast_exp2(__builtin_fmaf(sacc[kb][it], a.c, -m_run));
+                sacc[kb][it] = p;
+                rsp[it & 3] += p;
             }
+        l_run += halves_sum((rsp[0] + rsp[1]) + (rsp[2] + rsp[3]));
+        // P^T fragments (B operand): 16-key step c takes items 8*(c%2)..+7
+#pragma unroll
+        for (int c = 0; c < BN / 16; ++c) {
+            const f32x16& s = sacc[c >> 1];
+            const int o8 = (c & 1) * 8;
+            pf[c] = to_bf16x8(f32x8{s[o8 + 0], s[o8 + 1], s[o8 + 2], s[o8 + 3],
+                                    s[o8 + 4], s[o8 + 5], s[o8 + 6], s[o8 + 7]});
+        }
+    };
 
-            // P^T fragments (B operand): 16-key step c takes items 8*(c%2)..+7
-            bf16x8 pf[BN / 16];
+    // O^T[d][query] += V^T P^T
+    auto pv = [&](const unsigned char* vs, const bf16x8 (&pf)[BN / 16]) {
+        static_assert(BN == 64, "the transpose-read helper covers 4 steps of 16 keys");
+        const uint32_t vbase = lds_addr(vs);
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+            u32x2 vr8[8];
+            v_tr_reads<ROWB>(vbase + voff[0][db], vbase + voff[1][db], vr8);
 #pragma unroll
             for (int c = 0; c < BN / 16; ++c) {
-                const f32x16& s = sacc[c >> 1];
-                const int o8 = (c & 1) * 8;
-                pf[c] = to_bf16x8(f32x8{s[o8 + 0], s[o8 + 1], s[o8 + 2], s[o8 + 3],
-                                        s[o8 + 4], s[o8 + 5], s[o8 + 6], s[o8 + 7]});
-            }
-
-            // O^T[d][query] += V^T P^T
-            static_assert(BN == 64, "the transpose-read helper covers 4 steps of 16 keys");
-            const uint32_t vbase = lds_addr(vs);
-#pragma unroll
-            for (int db = 0; db < DBLK; ++db) {
-                u32x2 vr[8];
-                v_tr_reads<ROWB>(vbase + voff[0][db], vbase + voff[1][db], vr);
-#pragma unroll
-                for (int c = 0; c < BN / 16; ++c) {
-                    const u32x4 w = {vr[2 * c][0], vr[2 * c][1], vr[2 * c + 1][0], vr[2 * c + 1][1]};
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, w), pf[c], oacc[db], 0, 0, 0);
-                }
+                const u32x4 w = {vr8[2 * c][0], vr8[2 * c][1], vr8[2 * c + 1][0], vr8[2 * c + 1][1]};
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, w), pf[c], oacc[db], 0, 0, 0);
             }
         }
+    };
+
+    // ---- software pipeline over key tiles ----
+    // LDS holds a ring of NSTAGE K tiles and one of NSTAGE V tiles.  Step j
+    // computes S(j+1) = K(j+1) Q^T while it turns S(j) into probabilities and
+    // accumulates P(j) V(j).  K(t) is last read in step t-1 and V(t) in step
+    // t, so at the top of step j (after the barrier) the slots of K(j) and
+    // V(j-1) are free and receive K(j+3) and V(j+2): every tile is requested
+    // two steps before it is used.
+    auto kbuf = [&](int t) { return smem + (t % NSTAGE) * TILE_B; };
+    auto vbuf = [&](int t) { return smem + (NSTAGE + t % NSTAGE) * TILE_B; };
+
+    issue(kview, 0, kbuf(0));
+    issue(vview, 0, vbuf(0));
+    if (n_kt > 1) { issue(kview, 1, kbuf(1)); issue(vview, 1, vbuf(1)); }
+    if (n_kt > 2) issue(kview, 2, kbuf(2));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    f32x16 sa[BN / 32], sb[BN / 32];
+    if (wave_kt > 0) qk(kbuf(0), sa);
+
+    // one pipeline step; the loop below alternates the two score buffers so
+    // that S(j+1) never has to be copied into S(j)'s registers
+    int in_flight = 0;      // direct loads this thread issued in the previous step
+    auto step = [&](int j, f32x16 (&s_cur)[BN / 32], f32x16 (&s_next)[BN / 32]) {
+        // K(j+1) and V(j) were requested two steps ago: wait until only the
+        // previous step's requests may still be in flight, then make every
+        // wave's data visible (and every wave done with K(j), V(j-1))
+        if (in_flight == 2 * LOADS) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * LOADS) : "memory");
+        else if (in_flight == LOADS) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(LOADS) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // a bare barrier: the wait above already covers the loads this step
+        // needs, and a release fence here would also wait for the requests
+        // still in flight for later steps
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        in_flight = 0;
+        if (j + 3 < n_kt) { issue(kview, j + 3, kbuf(j + 3)); in_flight += LOADS; }
+        if (j + 2 < n_kt) { issue(vview, j + 2, vbuf(j + 2)); in_flight += LOADS; }
+
+        // this wave's last key tile holds its diagonal and needs the mask
+        const int last = wave_kt - 1;
+        if (j < last) {
+            // hot path: S(j+1) = K(j+1) Q^T interleaved with the softmax of S(j)
+            bf16x8 pf[BN / 16];
+            qk(kbuf(j + 1), s_next);
+            softmax(s_cur, j, false, pf);
+            // 16 x {one K fragment read, one MFMA, a slice of softmax VALU}
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // VALU
+            }
+            pv(vbuf(j), pf);
+        } else if (j == last) {
+            bf16x8 pf[BN / 16];
+            softmax(s_cur, j, true, pf);
+            pv(vbuf(j), pf);
+        }
+    };
+    for (int j = 0; j < n_kt; j += 2) {
+        step(j, sa, sb);
+        if (j + 1 < n_kt) step(j + 1, sb, sa);
     }
 
     // ---- epilogue: O = O^T / l, lane writes 4 consecutive dims per item group ----
@@ -375,7 +420,7 @@ hd_status launch_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v
     a.B = (uint32_t)B;
     a.Hkv = (uint32_t)Hkv;
     a.G = (uint32_t)(Hq / Hkv);
-    a.P = (a.G % 4 == 0) ? 4u : ((a.G % 2 == 0) ? 2u : 1u);
+    a.P = (a.G % 8 == 0) ? 8u : (a.G % 4 == 0) ? 4u : ((a.G % 2 == 0) ? 2u : 1u);
     a.n_hpacks = a.G / a.P;
     const uint32_t BT = MQ * (NW / a.P);
     a.n_qtiles = (a.len + BT - 1) / BT;

@@ -199,11 +199,12 @@ def test_prefill_exact_pins():
     om = hd.mix_attn(q, k, v, n, 1.0)
     assert torch.equal(ow[:, :n].view(torch.int16), vrep[:, :n].view(torch.int16))
     assert torch.equal(om[:, :1].view(torch.int16), vrep[:, :1].view(torch.int16))
-    # V == 1 -> O == 1 exactly (softmax rows sum to one)
+    # V == 1 -> O == 1 (softmax rows sum to one).  The weights enter P V as
+    # bf16 and the row sum in fp32, so O may sit one bf16 ulp (2^-8) from 1.
     ones = torch.ones_like(v)
     for fn in (hd.stream_attn, hd.mix_attn):
         o = fn(q, k, ones, n, 1.0)
-        assert torch.all(o == 1.0)
+        assert torch.all((o.float() - 1.0).abs() <= 2.0 ** -8)
 
 
 def test_prefill_stream_one_hot_pin():
