@@ -79,6 +79,11 @@ def bench_prefill(args, torch, hd, si):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # keep the GPU busy for ~0.5 s more so clocks have ramped before timing
+    t_end = time.perf_counter() + 0.5
+    while time.perf_counter() < t_end:
+        step()
+        torch.cuda.synchronize()
     # whole-step timing: K steps back to back, no events inside
     t0, t1 = _events(2)
     t0.record()
@@ -116,9 +121,10 @@ def bench_decode(args, torch, hd, si):
     reps = max(3, args.steps // 2)
     res = {}
     for mode, name in ((0, "within"), (1, "mix")):
-        for _ in range(2):
+        t_end = time.perf_counter() + 0.3
+        while time.perf_counter() < t_end:
             hd.decode_step(qn, kn, vn, kc, vc, tb, cfg.n, cfg.T, mode, cfg.scale, ws, out)
-        torch.cuda.synchronize()
+            torch.cuda.synchronize()
         e0, e1 = _events(2)
         e0.record()
         for _ in range(reps):
@@ -156,8 +162,10 @@ def bench_stack(args, torch, hd, si):
             hd.mix_attn(q, k, v, 1, cfg.scale, out=out1)
 
     def timeit(fn):
-        fn()
-        torch.cuda.synchronize()
+        t_end = time.perf_counter() + 0.2
+        while time.perf_counter() < t_end:
+            fn()
+            torch.cuda.synchronize()
         e0, e1 = _events(2)
         e0.record()
         for _ in range(reps):
@@ -236,6 +244,9 @@ def main():
                     help="seconds of CPU oracle work for cpu_baseline (0 to skip)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run one plain device copy (negation) of MIB MiB, the "
+                         "reference kernel for scaling HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -250,6 +261,16 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     hd.load()
+
+    if args.copy_calibration > 0:
+        nel = args.copy_calibration * (1 << 20) // 2
+        src = torch.ones(nel, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: {nel * 2} bytes read, {nel * 2} bytes written",
+              file=sys.stderr, flush=True)
+        del src, dst
 
     pf = bench_prefill(args, torch, hd, si)
     print(f"[bench] prefill done: step {pf['ms_step']:.4f} ms", file=sys.stderr, flush=True)

@@ -159,19 +159,22 @@ decode_attend_kernel(const DecodeArgs a) {
         for (int i = 0; i < DBLK; ++i) oacc[qb][i] = f32x16{};
     }
 
-    u32x4 kreg[K_CHUNKS];
-    u32x4 vreg[V_PER][4];
-    auto load_tile = [&](int t) {
+    // Tiles go global -> registers -> LDS.  Two register sets alternate so
+    // that two tiles (2 x 64 KB per workgroup) are in flight while a third is
+    // consumed from LDS.  Rows past the split end are clamped to its last
+    // row: the mask below gives them probability 0.
+    struct TileRegs {
+        u32x4 k[K_CHUNKS];
+        u32x4 v[V_PER][4];
+    };
+    const uint32_t last_key = key_end - 1;
+    auto load_tile = [&](int t, TileRegs& r) {
         const uint32_t k0 = key0 + (uint32_t)t * DT;
 #pragma unroll
         for (int i = 0; i < K_CHUNKS; ++i) {
             const int cidx = tid + i * DTHREADS;
-            const int row = cidx / CPR;
-            const int col = cidx % CPR;
-            const uint32_t key = k0 + row;
-            kreg[i] = key < key_end
-                ? *reinterpret_cast<const u32x4*>(kbase + key * kstep + col * 8)
-                : u32x4{0u, 0u, 0u, 0u};
+            const uint32_t key = min(k0 + cidx / CPR, last_key);
+            r.k[i] = *reinterpret_cast<const u32x4*>(kbase + key * kstep + (cidx % CPR) * 8);
         }
 #pragma unroll
         for (int i = 0; i < V_PER; ++i) {
@@ -179,21 +182,19 @@ decode_attend_kernel(const DecodeArgs a) {
             const int kq = task % (DT / 4);
             const int dq = task / (DT / 4);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const uint32_t key = k0 + 4 * kq + r;
-                vreg[i][r] = key < key_end
-                    ? *reinterpret_cast<const u32x4*>(vbase + key * kstep + dq * 8)
-                    : u32x4{0u, 0u, 0u, 0u};
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t key = min(k0 + 4 * kq + q, last_key);
+                r.v[i][q] = *reinterpret_cast<const u32x4*>(vbase + key * kstep + dq * 8);
             }
         }
     };
-    auto store_tile = [&]() {
+    auto store_tile = [&](const TileRegs& r) {
 #pragma unroll
         for (int i = 0; i < K_CHUNKS; ++i) {
             const int cidx = tid + i * DTHREADS;
             const int row = cidx / CPR;
             const int col = cidx % CPR;
-            *reinterpret_cast<u32x4*>(ks + row * KP + col * 8) = kreg[i];
+            *reinterpret_cast<u32x4*>(ks + row * KP + col * 8) = r.k[i];
         }
 #pragma unroll
         for (int i = 0; i < V_PER; ++i) {
@@ -201,94 +202,100 @@ decode_attend_kernel(const DecodeArgs a) {
             const int kq = task % (DT / 4);
             const int dq = task / (DT / 4);
             const int pos = vt_pos(kq);
+            // transpose 4 keys x 8 dims: row d of V^T gets the 4 keys' element d
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int w = j >> 1;
-                const int sh = (j & 1) * 16;
-                const uint32_t e0 = (vreg[i][0][w] >> sh) & 0xffffu;
-                const uint32_t e1 = (vreg[i][1][w] >> sh) & 0xffffu;
-                const uint32_t e2 = (vreg[i][2][w] >> sh) & 0xffffu;
-                const uint32_t e3 = (vreg[i][3][w] >> sh) & 0xffffu;
-                u32x2 pk = {e0 | (e1 << 16), e2 | (e3 << 16)};
-                *reinterpret_cast<u32x2*>(vt + (dq * 8 + j) * DVP + pos) = pk;
+            for (int w = 0; w < 4; ++w) {
+                u32x2 lo = {__builtin_amdgcn_perm(r.v[i][1][w], r.v[i][0][w], 0x05040100u),
+                            __builtin_amdgcn_perm(r.v[i][3][w], r.v[i][2][w], 0x05040100u)};
+                u32x2 hi = {__builtin_amdgcn_perm(r.v[i][1][w], r.v[i][0][w], 0x07060302u),
+                            __builtin_amdgcn_perm(r.v[i][3][w], r.v[i][2][w], 0x07060302u)};
+                *reinterpret_cast<u32x2*>(vt + (dq * 8 + 2 * w) * DVP + pos) = lo;
+                *reinterpret_cast<u32x2*>(vt + (dq * 8 + 2 * w + 1) * DVP + pos) = hi;
             }
         }
     };
 
-    load_tile(0);
-    for (int t = 0; t < n_tiles; ++t) {
-        store_tile();
-        __syncthreads();
-        if (t + 1 < n_tiles) load_tile(t + 1);
-
+    auto compute = [&](int t) {
         const uint32_t wk0 = key0 + (uint32_t)t * DT + wave * 32;   // this wave's first key
-        if (wk0 < key_end) {
-            f32x16 sacc[NQB];
-            const uint16_t* krow = ks + (wave * 32 + l32) * KP + hh * 8;
+        if (wk0 >= key_end) return;
+        f32x16 sacc[NQB];
+        const uint16_t* krow = ks + (wave * 32 + l32) * KP + hh * 8;
 #pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) sacc[qb] = f32x16{};
+        for (int qb = 0; qb < NQB; ++qb) sacc[qb] = f32x16{};
 #pragma unroll
-            for (int e = 0; e < DSTEPS; ++e) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + 16 * e);
+        for (int e = 0; e < DSTEPS; ++e) {
+            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + 16 * e);
 #pragma unroll
-                for (int qb = 0; qb < NQB; ++qb)
-                    sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][e], sacc[qb], 0, 0, 0);
-            }
+            for (int qb = 0; qb < NQB; ++qb)
+                sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][e], sacc[qb], 0, 0, 0);
+        }
 
-            bf16x8 pf[NQB][2];
+        bf16x8 pf[NQB][2];
 #pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) {
-                // keys past the view end or after the query (mixing, new token) -> -inf
-                if (wk0 + 31 > qidx[qb] || wk0 + 31 >= key_end) {
-#pragma unroll
-                    for (int it = 0; it < 16; ++it) {
-                        const uint32_t key = wk0 + 8 * (it >> 2) + 4 * hh + (it & 3);
-                        if (key > qidx[qb] || key >= key_end) sacc[qb][it] = -INFINITY;
-                    }
-                }
-                float mx = -INFINITY;
-#pragma unroll
-                for (int it = 0; it < 16; ++it) mx = fmaxf(mx, sacc[qb][it]);
-                mx = fmaxf(mx, xor32(mx));
-                const float m_new = fmaxf(m_run[qb], mx * a.c);
-                const float m_use = m_new == -INFINITY ? 0.f : m_new;
-                const float alpha = fast_exp2(m_run[qb] - m_use);
-                m_run[qb] = m_new;
-                float rs = 0.f;
+        for (int qb = 0; qb < NQB; ++qb) {
+            // keys past the view end or after the query (mixing, new token) -> -inf
+            if (wk0 + 31 > qidx[qb] || wk0 + 31 >= key_end) {
 #pragma unroll
                 for (int it = 0; it < 16; ++it) {
-                    const float p = fast_exp2(__builtin_fmaf(sacc[qb][it], a.c, -m_use));
-                    sacc[qb][it] = p;
-                    rs += p;
-                }
-                rs += xor32(rs);
-                l_run[qb] = l_run[qb] * alpha + rs;
-#pragma unroll
-                for (int i = 0; i < DBLK; ++i) oacc[qb][i] *= alpha;
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const int o8 = c * 8;
-                    u32x4 w;
-                    w[0] = pack_bf16x2(sacc[qb][o8 + 0], sacc[qb][o8 + 1]);
-                    w[1] = pack_bf16x2(sacc[qb][o8 + 2], sacc[qb][o8 + 3]);
-                    w[2] = pack_bf16x2(sacc[qb][o8 + 4], sacc[qb][o8 + 5]);
-                    w[3] = pack_bf16x2(sacc[qb][o8 + 6], sacc[qb][o8 + 7]);
-                    pf[qb][c] = __builtin_bit_cast(bf16x8, w);
+                    const uint32_t key = wk0 + 8 * (it >> 2) + 4 * hh + (it & 3);
+                    if (key > qidx[qb] || key >= key_end) sacc[qb][it] = -INFINITY;
                 }
             }
+            float mx = -INFINITY;
 #pragma unroll
-            for (int db = 0; db < DBLK; ++db) {
-                const uint16_t* vrow = vt + (db * 32 + l32) * DVP + wave * 32 + hh * 8;
+            for (int it = 0; it < 16; ++it) mx = fmaxf(mx, sacc[qb][it]);
+            mx = halves_max(mx);
+            const float m_new = fmaxf(m_run[qb], mx * a.c);
+            const float m_use = m_new == -INFINITY ? 0.f : m_new;
+            const float alpha = fast_exp2(m_run[qb] - m_use);
+            m_run[qb] = m_new;
+            float rsp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vrow + 16 * c);
+            for (int it = 0; it < 16; ++it) {
+                const float p = fast_exp2(__builtin_fmaf(sacc[qb][it], a.c, -m_use));
+                sacc[qb][it] = p;
+                rsp[it & 3] += p;
+            }
+            l_run[qb] = l_run[qb] * alpha + halves_sum((rsp[0] + rsp[1]) + (rsp[2] + rsp[3]));
 #pragma unroll
-                    for (int qb = 0; qb < NQB; ++qb)
-                        oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][c], oacc[qb][db], 0, 0, 0);
-                }
+            for (int i = 0; i < DBLK; ++i) oacc[qb][i] *= alpha;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const int o8 = c * 8;
+                pf[qb][c] = to_bf16x8(f32x8{sacc[qb][o8 + 0], sacc[qb][o8 + 1], sacc[qb][o8 + 2],
+                                            sacc[qb][o8 + 3], sacc[qb][o8 + 4], sacc[qb][o8 + 5],
+                                            sacc[qb][o8 + 6], sacc[qb][o8 + 7]});
             }
         }
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+            const uint16_t* vrow = vt + (db * 32 + l32) * DVP + wave * 32 + hh * 8;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vrow + 16 * c);
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb)
+                    oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][c], oacc[qb][db], 0, 0, 0);
+            }
+        }
+    };
+
+    TileRegs ra, rb;
+    load_tile(0, ra);
+    if (n_tiles > 1) load_tile(1, rb);
+    for (int t = 0; t < n_tiles; t += 2) {
+        store_tile(ra);
         __syncthreads();
+        if (t + 2 < n_tiles) load_tile(t + 2, ra);
+        compute(t);
+        __syncthreads();
+        if (t + 1 < n_tiles) {
+            store_tile(rb);
+            __syncthreads();
+            if (t + 3 < n_tiles) load_tile(t + 3, rb);
+            compute(t + 1);
+            __syncthreads();
+        }
     }
 
     // ---- merge the 4 waves' partial softmax states through LDS ----
