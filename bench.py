@@ -52,6 +52,25 @@ def decode_bytes(S, n, T, Hkv, D):
     return S * (T + 1) * n * Hkv * D * 2 * 2
 
 
+def measured_traffic(kernel, src):
+    """HBM bytes per launch of `kernel` (read + write, averaged over the
+    within-stream and mixing launches) from the rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary in profiles/traffic.json -- only if that summary was
+    taken on the current kernel source, else None."""
+    import hashlib
+    try:
+        t = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+        cur = hashlib.sha256(open(os.path.join(ROOT, "sequence_length_latent_amd", "csrc", src),
+                                  "rb").read()).hexdigest()
+        key = "prefill_source_sha256" if src == "prefill.hip" else "decode_source_sha256"
+        if t.get(key) != cur:
+            return None
+        per = t[kernel]
+        return round(sum(v["read"] + v["write"] for v in per.values()) / len(per))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def _events(k):
     import torch
     return [torch.cuda.Event(enable_timing=True) for _ in range(k)]
@@ -327,7 +346,10 @@ def main():
         "roofline": {
             "kernel": "sfa_prefill_kernel<128> (both layers; 2 launches per step)",
             "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+            "traffic": measured_traffic("sfa_prefill_kernel_n4", "prefill.hip"),
+            "traffic_unit": "bytes per launch (HBM read + write)",
+            "algorithmic_flop_per_launch": round(flops / 2),
         },
         "kernels": kernels,
     }
@@ -343,6 +365,7 @@ def main():
             line["decode"][name] = {"ms": round(dec[name], 4), "achieved": round(gbs, 1),
                                     "unit": "GB/s", "peak": PEAK_HBM_GBS,
                                     "frac": round(gbs / PEAK_HBM_GBS, 4)}
+        line["decode"]["traffic"] = measured_traffic("decode_attend_kernel", "decode.hip")
     if stack:
         line["stack"] = stack
     line["cpu_baseline"] = cpu
