@@ -15,21 +15,26 @@
 // key tiles of its own stream that are not in its future: nothing is computed
 // for the (n-1)/n of pairs the mask removes.
 //
-// Workgroup = 4 waves.  Each wave owns 32 query rows of one query head and
-// computes S^T = K Q^T and O^T += V^T P^T with the gfx950 bf16 matrix op
-// v_mfma_f32_32x32x16_bf16 (fp32 accumulate).  Keeping S transposed puts one
-// query per lane (pair of lanes), so row max / row sum are per-lane values
+// Work items are (query tile, batch, view, KV head, head pack), listed longest
+// causal extent first.  The grid is persistent, one workgroup per compute
+// unit: workgroup b takes item r*grid + b on even rounds r and
+// r*grid + (grid-1-b) on odd rounds, which evens out the triangular costs.
+// While a workgroup normalises and stores one item's output, the Q fragments
+// and first K/V tiles of its next item are already on their way.
+//
+// Workgroup = 8 waves (2 per SIMD).  Each wave owns 32 query rows of one query
+// head and computes S^T = K Q^T and O^T += V^T P^T with the gfx950 bf16 matrix
+// op v_mfma_f32_32x32x16_bf16 (fp32 accumulate).  Keeping S transposed puts
+// one query per lane (pair of lanes), so row max / row sum are per-lane values
 // plus one exchange with the other half-wave, and the probabilities leave the
 // accumulator already in the B-operand layout of the second product.
-// GQA: the query heads sharing a KV head are packed into one workgroup (up to
-// 4, one per wave) so each K/V tile is staged once in LDS for all of them and
-// every wave has the same causal extent.
+// GQA: the query heads sharing a KV head are packed into one workgroup so each
+// K/V tile is staged once in LDS for all of them.
 //
-// K is staged in LDS row-major with a 16-byte row pad (conflict-free 16-byte
-// reads); V is staged transposed ([d][key]) with keys permuted inside each
-// 16-key group so that one 16-byte LDS read yields exactly the 8 keys a lane
-// needs for the V^T operand.  Tiles are double-buffered in LDS with a
-// register prefetch of the next tile, one barrier per tile.
+// K and V tiles of 64 keys are copied global -> LDS by direct loads
+// (global_load_lds, 16 bytes per lane) into a two-deep ring, row-major with an
+// XOR swizzle of the 16-byte chunks.  K fragments are 16-byte LDS reads; the
+// V^T operand comes from transpose reads (ds_read_b64_tr_b16).
 #include "common.h"
 
 namespace hdsfa {
@@ -39,7 +44,7 @@ namespace {
 constexpr int BN = 64;       // keys per tile
 constexpr int MQ = 32;       // query rows per wave
 constexpr int NW = 8;        // waves per workgroup (2 per SIMD)
-constexpr int NSTAGE = 3;    // LDS ring depth for K and for V tiles
+constexpr int NSTAGE = 2;    // LDS ring depth for K and for V tiles
 constexpr int THREADS = NW * kWave;
 
 struct PrefillArgs {
@@ -61,6 +66,7 @@ struct PrefillArgs {
     uint32_t P;          // query heads packed per workgroup (1, 2, 4 or 8)
     uint32_t n_hpacks;   // G / P
     uint32_t n_qtiles;   // ceil(len / (MQ * NW / P))
+    uint32_t n_items;    // n_qtiles * B * groups * Hkv * n_hpacks
     float c;             // softmax scale * log2(e)
 };
 
@@ -111,13 +117,13 @@ __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2,
 sfa_prefill_kernel(const PrefillArgs a) {
     constexpr int ROWB = D * 2;                // bytes per K/V row
     constexpr int TILE_B = BN * ROWB;          // one K (or V) tile
-    constexpr int STAGE_B = 2 * TILE_B;        // K tile then V tile
     constexpr int LOADS = TILE_B / (THREADS * 16);   // 16-byte direct loads per thread per tile
     constexpr int DSTEPS = D / 16;             // k-steps of the score product
     constexpr int DBLK = D / 32;               // 32-row blocks of O^T
     static_assert(TILE_B % (THREADS * 16) == 0, "tile/thread mismatch");
 
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * STAGE_B];   // K ring, V ring
+    constexpr int QW_B = DSTEPS * 1024;        // one wave's Q fragments
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * NSTAGE * TILE_B + NW * QW_B];   // K ring, V ring, Q
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -125,51 +131,64 @@ sfa_prefill_kernel(const PrefillArgs a) {
     const int l32 = lane & 31;
     const int hh = lane >> 5;                  // half-wave index
 
-    // ---- work item (longest query tiles first) ----
-    uint32_t id = blockIdx.x;
-    const uint32_t per_tile = a.B * a.groups * a.Hkv * a.n_hpacks;
-    const uint32_t qtile = a.n_qtiles - 1 - id / per_tile;
-    id %= per_tile;
-    const uint32_t hp = id % a.n_hpacks;
-    id /= a.n_hpacks;
-    const uint32_t kvh = id % a.Hkv;
-    id /= a.Hkv;
-    const uint32_t grp = id % a.groups;
-    const uint32_t b = id / a.groups;
-
     const int qblocks = NW / a.P;
-    const int BT = MQ * qblocks;               // query rows per workgroup
-    const uint32_t head = kvh * a.G + hp * a.P + (wave % a.P);
-    const uint32_t q0 = qtile * BT + (wave / a.P) * MQ;
+    const uint32_t BT = MQ * qblocks;          // query rows per work item
+    const uint32_t per_tile = a.B * a.groups * a.Hkv * a.n_hpacks;
 
-    const uint16_t* qbase = a.q + b * a.q_batch + grp * a.q_group + (uint64_t)head * D;
-    uint16_t* obase = a.o + b * a.q_batch + grp * a.q_group + (uint64_t)head * D;
-    const char* kview = reinterpret_cast<const char*>(a.k + b * a.kv_batch + grp * a.kv_group + (uint64_t)kvh * D);
-    const char* vview = reinterpret_cast<const char*>(a.v + b * a.kv_batch + grp * a.kv_group + (uint64_t)kvh * D);
+    bf16x8 qf[DSTEPS];                         // Q fragments of the current item
+    f32x16 oacc[DBLK];                         // O^T accumulators
+    float m_run, l_run;   // running max (log2 units, already * c) and sum of exp2
 
-    const uint32_t wg_end = min(a.len, (qtile + 1) * (uint32_t)BT);
-    const int n_kt = (int)((wg_end + BN - 1) / BN);
-    const uint32_t wave_end = min(a.len, q0 + MQ);       // exclusive
-    const int wave_kt = q0 < a.len ? (int)((wave_end + BN - 1) / BN) : 0;
-
-    // ---- Q fragments: lane holds query q0+l32, dims 16e + 8hh .. +7 ----
-    const uint32_t qi = q0 + l32;
-    bf16x8 qf[DSTEPS];
-    {
-        const bool ok = qi < a.len;
-        const u32x4* src = reinterpret_cast<const u32x4*>(qbase + (uint64_t)qi * a.q_row);
-#pragma unroll
-        for (int e = 0; e < DSTEPS; ++e) {
-            u32x4 w = ok ? src[2 * e + hh] : u32x4{0u, 0u, 0u, 0u};
-            qf[e] = __builtin_bit_cast(bf16x8, w);
-        }
-    }
-
-    f32x16 oacc[DBLK];
-#pragma unroll
-    for (int i = 0; i < DBLK; ++i) oacc[i] = f32x16{};
-    float m_run = -INFINITY;   // running max, in log2 units (already * c)
-    float l_run = 0.f;         // running sum of exp2
+    // ---- work items ----
+    // Only what the key loop needs stays live across an item (the views, the
+    // tile counts and the lane's query row); the Q and O row addresses are
+    // recomputed from the item index where they are used.
+    struct Item {
+        uint32_t id;
+        const char* kview;
+        const char* vview;
+        int n_kt;             // key tiles the workgroup visits
+        int wave_kt;          // key tiles this wave needs
+        uint32_t qi;          // this lane's query row in the view
+    };
+    // (batch, view, query head) offset of an item, in elements, and its first row
+    auto item_head = [&](uint32_t id, uint32_t& q0) -> uint64_t {
+        const uint32_t qtile = a.n_qtiles - 1 - id / per_tile;
+        id %= per_tile;
+        const uint32_t hp = id % a.n_hpacks;
+        id /= a.n_hpacks;
+        const uint32_t kvh = id % a.Hkv;
+        id /= a.Hkv;
+        const uint32_t grp = id % a.groups;
+        const uint32_t b = id / a.groups;
+        q0 = qtile * BT + (wave / a.P) * MQ;
+        return b * a.q_batch + grp * a.q_group + (uint64_t)(kvh * a.G + hp * a.P + (wave % a.P)) * D;
+    };
+    auto make_item = [&](uint32_t id) -> Item {
+        Item it;
+        it.id = id;
+        const uint32_t qtile = a.n_qtiles - 1 - id / per_tile;
+        uint32_t r = id % per_tile;
+        r /= a.n_hpacks;
+        const uint32_t kvh = r % a.Hkv;
+        r /= a.Hkv;
+        const uint32_t grp = r % a.groups;
+        const uint32_t b = r / a.groups;
+        it.kview = reinterpret_cast<const char*>(a.k + b * a.kv_batch + grp * a.kv_group + (uint64_t)kvh * D);
+        it.vview = reinterpret_cast<const char*>(a.v + b * a.kv_batch + grp * a.kv_group + (uint64_t)kvh * D);
+        const uint32_t wg_end = min(a.len, (qtile + 1) * BT);
+        it.n_kt = (int)((wg_end + BN - 1) / BN);
+        const uint32_t q0 = qtile * BT + (wave / a.P) * MQ;
+        const uint32_t wave_end = min(a.len, q0 + MQ);       // exclusive
+        it.wave_kt = q0 < a.len ? (int)((wave_end + BN - 1) / BN) : 0;
+        it.qi = q0 + l32;
+        return it;
+    };
+    // item taken in round r (snake order over the grid)
+    auto item_at = [&](uint32_t r) -> uint32_t {
+        const uint32_t g = gridDim.x;
+        return r * g + ((r & 1u) ? (g - 1u - blockIdx.x) : blockIdx.x);
+    };
 
     // ---- direct global->LDS tile loads ----
     // Load j of this wave fills LDS bytes [(wave*LOADS + j)*1024, +1024) of a
@@ -202,6 +221,70 @@ sfa_prefill_kernel(const PrefillArgs a) {
                 (void __attribute__((address_space(3)))*)(buf + (wave * LOADS + j) * 1024), 16, 0, 0);
         }
     };
+    auto kbuf = [&](int t) { return smem + (t & 1) * TILE_B; };
+    auto vbuf = [&](int t) { return smem + (NSTAGE + (t & 1)) * TILE_B; };
+    // Q fragments of an item, global -> this wave's LDS Q area: load e, lane
+    // l brings query row q0 + l%32 (clamped into the view; rows past its end
+    // are never stored), dims 16e + 8(l/32) .. +7, to +1024e + 16l.  The
+    // area is read once at the start of the item, so the next item's Q can be
+    // requested any time after that.
+    unsigned char* const qlds = smem + 2 * NSTAGE * TILE_B + wave * QW_B;
+    auto issue_q = [&](uint32_t id) {
+        uint32_t q0;
+        const uint64_t hoff = item_head(id, q0);
+        const char* src = reinterpret_cast<const char*>(
+            a.q + hoff + (uint64_t)min(q0 + l32, a.len - 1u) * a.q_row);
+#pragma unroll
+        for (int e = 0; e < DSTEPS; ++e)
+            __builtin_amdgcn_global_load_lds(
+                (const void __attribute__((address_space(1)))*)(src + (2 * e + hh) * 16),
+                (void __attribute__((address_space(3)))*)(qlds + e * 1024), 16, 0, 0);
+    };
+
+    // ---- output ----
+    // O = O^T / l leaves through 2 KB per wave of V slot 1, which no wave
+    // reads or fills between the barrier that ends an item and the first step
+    // of the next: per 32-dim block the wave writes its 32 rows x 64 bytes
+    // (16-byte chunks XOR-swizzled by row), reads them back 4 lanes per row,
+    // and stores whole 64-byte row pieces.
+    auto store_out = [&](uint32_t id, uint32_t qi) {
+        uint32_t q0;
+        uint16_t* obase = a.o + item_head(id, q0);
+        const float inv = 1.f / l_run;         // unused (never stored) where qi >= len
+        if constexpr (TILE_B >= NW * 2048) {
+            unsigned char* stg = vbuf(1) + wave * 2048;
+            const uint32_t rr = (uint32_t)lane >> 2, rc = (uint32_t)lane & 3u;
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const u32x2 w = {pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv),
+                                     pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+                    const uint32_t pc = (uint32_t)g ^ (((uint32_t)l32 >> 2) & 3u);
+                    *reinterpret_cast<u32x2*>(stg + l32 * 64 + pc * 16 + hh * 8) = w;
+                }
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t r = rr + 16u * h;
+                    const u32x4 w = *reinterpret_cast<const u32x4*>(stg + r * 64 + ((rc ^ ((r >> 2) & 3u)) << 4));
+                    if (q0 + r < a.len)
+                        *reinterpret_cast<u32x4*>(obase + (uint64_t)(q0 + r) * a.q_row + db * 32 + rc * 8) = w;
+                }
+            }
+        } else if (qi < a.len) {
+            // 4 consecutive dims per lane and item group
+            uint16_t* orow = obase + (uint64_t)qi * a.q_row;
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int d = db * 32 + 8 * g + 4 * hh;
+                    u32x2 w = {pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv),
+                               pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+                    *reinterpret_cast<u32x2*>(orow + d) = w;
+                }
+        }
+    };
 
     // ---- per-lane LDS read offsets (independent of the tile) ----
     // K (A operand of S^T = K Q^T): row kb*32 + l32, logical chunk 2e + hh.
@@ -229,6 +312,7 @@ sfa_prefill_kernel(const PrefillArgs a) {
         }
     }
 
+
     // S^T[key][query] = K Q^T for the two 32-key blocks of a tile
     auto qk = [&](const unsigned char* ks, f32x16 (&sacc)[BN / 32]) {
 #pragma unroll
@@ -244,7 +328,7 @@ sfa_prefill_kernel(const PrefillArgs a) {
 
     // online softmax of one tile's scores; returns the P^T operands.  The
     // causal mask is needed only on a wave's last (diagonal) tile.
-    auto softmax = [&](f32x16 (&sacc)[BN / 32], int kt, bool diag, bf16x8 (&pf)[BN / 16]) {
+    auto softmax = [&](f32x16 (&sacc)[BN / 32], int kt, bool diag, uint32_t qi, bf16x8 (&pf)[BN / 16]) {
         if (diag) {
             const uint32_t k0 = (uint32_t)kt * BN;
 #pragma unroll
@@ -311,50 +395,45 @@ sfa_prefill_kernel(const PrefillArgs a) {
     };
 
     // ---- software pipeline over key tiles ----
-    // LDS holds a ring of NSTAGE K tiles and one of NSTAGE V tiles.  Step j
-    // computes S(j+1) = K(j+1) Q^T while it turns S(j) into probabilities and
-    // accumulates P(j) V(j).  K(t) is last read in step t-1 and V(t) in step
-    // t, so at the top of step j (after the barrier) the slots of K(j) and
-    // V(j-1) are free and receive K(j+3) and V(j+2): every tile is requested
-    // two steps before it is used.
-    auto kbuf = [&](int t) { return smem + (t % NSTAGE) * TILE_B; };
-    auto vbuf = [&](int t) { return smem + (NSTAGE + t % NSTAGE) * TILE_B; };
-
-    issue(kview, 0, kbuf(0));
-    issue(vview, 0, vbuf(0));
-    if (n_kt > 1) { issue(kview, 1, kbuf(1)); issue(vview, 1, vbuf(1)); }
-    if (n_kt > 2) issue(kview, 2, kbuf(2));
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    f32x16 sa[BN / 32], sb[BN / 32];
-    if (wave_kt > 0) qk(kbuf(0), sa);
-
-    // one pipeline step; the loop below alternates the two score buffers so
-    // that S(j+1) never has to be copied into S(j)'s registers
-    int in_flight = 0;      // direct loads this thread issued in the previous step
-    auto step = [&](int j, f32x16 (&s_cur)[BN / 32], f32x16 (&s_next)[BN / 32]) {
-        // K(j+1) and V(j) were requested two steps ago: wait until only the
-        // previous step's requests may still be in flight, then make every
-        // wave's data visible (and every wave done with K(j), V(j-1))
-        if (in_flight == 2 * LOADS) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * LOADS) : "memory");
-        else if (in_flight == LOADS) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(LOADS) : "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        // a bare barrier: the wait above already covers the loads this step
-        // needs, and a release fence here would also wait for the requests
-        // still in flight for later steps
+    // Step j computes S(j+1) = K(j+1) Q^T while it turns S(j) into
+    // probabilities and accumulates P(j) V(j).  K(t) is last read in step t-1
+    // and V(t) in step t, so after the barrier at the top of step j the slots
+    // of K(j) and V(j-1) are free and receive K(j+2) and V(j+1): every tile is
+    // requested one step before it is used.  The final step F of an item reads
+    // no K tile and only V(F): there the next item's Q, K(0), K(1) and, if
+    // its slot is free (F odd), V(0) are requested.
+    auto step = [&](int j, f32x16 (&s_cur)[BN / 32], f32x16 (&s_next)[BN / 32],
+                    const Item& cur, uint32_t nid, bool more) {
+        // K(j+1) and V(j) were requested in the previous step; a bare barrier
+        // then makes every wave's copies visible (the wait above already
+        // covers them, and a release fence would add nothing)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        in_flight = 0;
-        if (j + 3 < n_kt) { issue(kview, j + 3, kbuf(j + 3)); in_flight += LOADS; }
-        if (j + 2 < n_kt) { issue(vview, j + 2, vbuf(j + 2)); in_flight += LOADS; }
+        if (j + 2 < cur.n_kt) issue(cur.kview, j + 2, kbuf(j + 2));
+        if (j + 1 < cur.n_kt) issue(cur.vview, j + 1, vbuf(j + 1));
+        // the previous item's output (its LDS reads finish before the Q area
+        // can be refilled below)
+        if (j == cur.n_kt - 1 && more) {
+            // an opaque copy of the index keeps the address arithmetic here
+            // (it is loop-invariant) from being hoisted and held in registers
+            // across the whole key loop
+            uint32_t id2;
+            asm volatile("s_mov_b32 %0, %1" : "=s"(id2) : "s"(nid));
+            const Item nx = make_item(id2);
+            issue_q(id2);
+            issue(nx.kview, 0, kbuf(0));
+            if (nx.n_kt > 1) issue(nx.kview, 1, kbuf(1));
+            if (j & 1) issue(nx.vview, 0, vbuf(0));
+        }
 
         // this wave's last key tile holds its diagonal and needs the mask
-        const int last = wave_kt - 1;
+        const int last = cur.wave_kt - 1;
         if (j < last) {
             // hot path: S(j+1) = K(j+1) Q^T interleaved with the softmax of S(j)
             bf16x8 pf[BN / 16];
             qk(kbuf(j + 1), s_next);
-            softmax(s_cur, j, false, pf);
+            softmax(s_cur, j, false, cur.qi, pf);
             // 16 x {one K fragment read, one MFMA, a slice of softmax VALU}
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
@@ -365,29 +444,63 @@ sfa_prefill_kernel(const PrefillArgs a) {
             pv(vbuf(j), pf);
         } else if (j == last) {
             bf16x8 pf[BN / 16];
-            softmax(s_cur, j, true, pf);
+            softmax(s_cur, j, true, cur.qi, pf);
             pv(vbuf(j), pf);
         }
     };
-    for (int j = 0; j < n_kt; j += 2) {
-        step(j, sa, sb);
-        if (j + 1 < n_kt) step(j + 1, sb, sa);
-    }
 
-    // ---- epilogue: O = O^T / l, lane writes 4 consecutive dims per item group ----
-    if (qi < a.len) {
-        const float inv = 1.f / l_run;
-        uint16_t* orow = obase + (uint64_t)qi * a.q_row;
+    // ---- persistent loop over this workgroup's work items ----
+    uint32_t round = 0;
+    const uint32_t first = item_at(0);
+    if (first >= a.n_items) return;            // uniform over the workgroup
+    Item cur = make_item(first);
+    issue_q(first);
+    issue(cur.kview, 0, kbuf(0));
+    issue(cur.vview, 0, vbuf(0));
+    if (cur.n_kt > 1) issue(cur.kview, 1, kbuf(1));
+    for (;;) {
+        const uint32_t nid = item_at(round + 1);
+        const bool more = nid < a.n_items;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
 #pragma unroll
-        for (int db = 0; db < DBLK; ++db)
+        for (int e = 0; e < DSTEPS; ++e)
+            qf[e] = *reinterpret_cast<const bf16x8*>(qlds + e * 1024 + lane * 16);
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d = db * 32 + 8 * g + 4 * hh;
-                u32x2 w = {pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv),
-                           pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
-                *reinterpret_cast<u32x2*>(orow + d) = w;
-            }
+        for (int i = 0; i < DBLK; ++i) oacc[i] = f32x16{};
+        m_run = -INFINITY;
+        l_run = 0.f;
+        f32x16 sa[BN / 32], sb[BN / 32];
+        if (cur.wave_kt > 0) qk(kbuf(0), sa);
+        for (int j = 0; j < cur.n_kt; j += 2) {
+            step(j, sa, sb, cur, nid, more);
+            if (j + 1 < cur.n_kt) step(j + 1, sb, sa, cur, nid, more);
+        }
+        // every wave has finished reading this item's tiles: the ring is free
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        // V(0) of the next item, unless the final step (odd F) already sent it
+        if (more && (cur.n_kt & 1)) issue(make_item(nid).vview, 0, vbuf(0));
+        store_out(cur.id, cur.qi);
+        if (!more) break;
+        cur = make_item(nid);
+        ++round;
     }
+}
+
+// compute units of the current device (the persistent grid size)
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int c = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
+    if (c <= 0) {
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+            c = 256;
+        __atomic_store_n(&cached[dev], c, __ATOMIC_RELAXED);
+    }
+    return c;
 }
 
 hd_status launch_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -426,8 +539,10 @@ hd_status launch_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v
     a.n_qtiles = (a.len + BT - 1) / BT;
     a.c = scale * kLog2e;
 
-    const uint64_t blocks = (uint64_t)a.n_qtiles * a.B * a.groups * a.Hkv * a.n_hpacks;
-    if (blocks > 0x7fffffffULL) return HD_ERR_UNSUPPORTED;
+    const uint64_t items = (uint64_t)a.n_qtiles * a.B * a.groups * a.Hkv * a.n_hpacks;
+    if (items > 0x7fffffffULL) return HD_ERR_UNSUPPORTED;
+    a.n_items = (uint32_t)items;
+    const uint64_t blocks = items < (uint64_t)device_cus() ? items : (uint64_t)device_cus();
     if (D == 128)
         sfa_prefill_kernel<128><<<dim3((uint32_t)blocks), dim3(THREADS), 0, stream>>>(a);
     else
