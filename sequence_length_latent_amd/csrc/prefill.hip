@@ -35,7 +35,17 @@
 // (global_load_lds, 16 bytes per lane) into a two-deep ring, row-major with an
 // XOR swizzle of the 16-byte chunks.  K fragments are 16-byte LDS reads; the
 // V^T operand comes from transpose reads (ds_read_b64_tr_b16).
+//
+// Per key tile a wave runs two phases: the online softmax (vector ALU) and
+// the matrix phase (the score product of the next tile and the value product
+// of this one).  The matrix phase is generated assembly (prefill_asm.h) that
+// issues every LDS operand read several MFMAs ahead of its use; the two waves
+// that share a SIMD run the phases half a tile apart, so one wave's softmax
+// overlaps the other's matrix products.
 #include "common.h"
+#include "prefill_asm.h"
+
+#include <type_traits>
 
 namespace hdsfa {
 
@@ -82,30 +92,6 @@ template <int D>
 __device__ __forceinline__ uint32_t swz(uint32_t row) {
     if constexpr (D == 128) return ((row & 3u) << 2) | ((row >> 2) & 3u);
     else return (((row >> 1) & 1u) << 2) | ((row >> 2) & 3u);
-}
-
-// Eight transpose reads of V for one 32-dim block: the two key quads (rd = 0,
-// 1) of each of the four 16-key steps c (immediate offsets c * 16 rows).  The
-// reads are issued from inline assembly so that the compiler does not order
-// them behind the asynchronous global->LDS loads of the next tile, which
-// target the other LDS stage; the block waits for its own results before it
-// returns, so every output register is complete when the asm ends.
-template <int ROWB>
-__device__ __forceinline__ void v_tr_reads(uint32_t a0, uint32_t a1, u32x2 (&r)[8]) {
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %8\n\t"
-        "ds_read_b64_tr_b16 %1, %9\n\t"
-        "ds_read_b64_tr_b16 %2, %8 offset:%10\n\t"
-        "ds_read_b64_tr_b16 %3, %9 offset:%10\n\t"
-        "ds_read_b64_tr_b16 %4, %8 offset:%11\n\t"
-        "ds_read_b64_tr_b16 %5, %9 offset:%11\n\t"
-        "ds_read_b64_tr_b16 %6, %8 offset:%12\n\t"
-        "ds_read_b64_tr_b16 %7, %9 offset:%12\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]),
-          "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
-        : "v"(a0), "v"(a1), "i"(16 * ROWB), "i"(32 * ROWB), "i"(48 * ROWB)
-        : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -313,19 +299,6 @@ sfa_prefill_kernel(const PrefillArgs a) {
     }
 
 
-    // S^T[key][query] = K Q^T for the two 32-key blocks of a tile
-    auto qk = [&](const unsigned char* ks, f32x16 (&sacc)[BN / 32]) {
-#pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb) sacc[kb] = f32x16{};
-#pragma unroll
-        for (int e = 0; e < DSTEPS; ++e)
-#pragma unroll
-            for (int kb = 0; kb < BN / 32; ++kb) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + kb * 32 * ROWB + koff[e]);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[e], sacc[kb], 0, 0, 0);
-            }
-    };
-
     // online softmax of one tile's scores; returns the P^T operands.  The
     // causal mask is needed only on a wave's last (diagonal) tile.
     auto softmax = [&](f32x16 (&sacc)[BN / 32], int kt, bool diag, uint32_t qi, bf16x8 (&pf)[BN / 16]) {
@@ -377,44 +350,39 @@ sfa_prefill_kernel(const PrefillArgs a) {
         }
     };
 
-    // O^T[d][query] += V^T P^T
-    auto pv = [&](const unsigned char* vs, const bf16x8 (&pf)[BN / 16]) {
-        static_assert(BN == 64, "the transpose-read helper covers 4 steps of 16 keys");
-        const uint32_t vbase = lds_addr(vs);
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) {
-            u32x2 vr8[8];
-            v_tr_reads<ROWB>(vbase + voff[0][db], vbase + voff[1][db], vr8);
-#pragma unroll
-            for (int c = 0; c < BN / 16; ++c) {
-                const u32x4 w = {vr8[2 * c][0], vr8[2 * c][1], vr8[2 * c + 1][0], vr8[2 * c + 1][1]};
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, w), pf[c], oacc[db], 0, 0, 0);
-            }
-        }
-    };
-
     // ---- software pipeline over key tiles ----
-    // Step j computes S(j+1) = K(j+1) Q^T while it turns S(j) into
-    // probabilities and accumulates P(j) V(j).  K(t) is last read in step t-1
-    // and V(t) in step t, so after the barrier at the top of step j the slots
-    // of K(j) and V(j-1) are free and receive K(j+2) and V(j+1): every tile is
-    // requested one step before it is used.  The final step F of an item reads
-    // no K tile and only V(F): there the next item's Q, K(0), K(1) and, if
-    // its slot is free (F odd), V(0) are requested.
-    auto step = [&](int j, f32x16 (&s_cur)[BN / 32], f32x16 (&s_next)[BN / 32],
-                    const Item& cur, uint32_t nid, bool more) {
-        // K(j+1) and V(j) were requested in the previous step; a bare barrier
-        // then makes every wave's copies visible (the wait above already
-        // covers them, and a release fence would add nothing)
+    // Two phases per key tile m:
+    //   A(m): online softmax of S(m) into P(m) (VALU);
+    //   B(m): S(m+1) = K(m+1) Q^T and O^T += V(m)^T P(m)^T (32 MFMAs at
+    //         head_dim 128, LDS operands read ahead; generated assembly).
+    // The two waves sharing a SIMD run them half a step apart: waves 0-3 do
+    // A(m), barrier, B(m); waves 4-7 do barrier, A(m), B(m) ... so one wave's
+    // softmax overlaps the other's matrix products.  Barrier m (one per key
+    // tile, reached by every wave) orders the LDS ring: both groups read
+    // K(m+1) and V(m) between barriers m and m+1, so at barrier m the slots of
+    // K(m) and V(m-1) are free and receive K(m+2) and V(m+1), waited for at
+    // barrier m+1.  In the final interval F no K tile is read and only V(F):
+    // there the next item's Q, K(0), K(1) and, if its slot is free (F odd),
+    // V(0) are requested.
+    const int wgrp = __builtin_amdgcn_readfirstlane(wave) >> 2;   // one wave of each group per SIMD
+    f32x16 sc[BN / 32];                        // S(m) (scores), then P(m) in place
+    bf16x8 pf[BN / 16];                        // P(m) as B operands of the value product
+    const uint32_t lds0 = lds_addr(smem);
+    uint32_t KA[DSTEPS], VA[2 * DBLK];         // LDS addresses of this lane's K / V reads
+#pragma unroll
+    for (int e = 0; e < DSTEPS; ++e) KA[e] = lds0 + koff[e];
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd)
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) VA[rd * DBLK + db] = lds0 + voff[rd][db];
+
+    auto barrier_step = [&](int m, const Item& cur, uint32_t nid, bool more) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (j + 2 < cur.n_kt) issue(cur.kview, j + 2, kbuf(j + 2));
-        if (j + 1 < cur.n_kt) issue(cur.vview, j + 1, vbuf(j + 1));
-        // the previous item's output (its LDS reads finish before the Q area
-        // can be refilled below)
-        if (j == cur.n_kt - 1 && more) {
+        if (m + 2 < cur.n_kt) issue(cur.kview, m + 2, kbuf(m + 2));
+        if (m + 1 < cur.n_kt) issue(cur.vview, m + 1, vbuf(m + 1));
+        if (m == cur.n_kt - 1 && more) {
             // an opaque copy of the index keeps the address arithmetic here
             // (it is loop-invariant) from being hoisted and held in registers
             // across the whole key loop
@@ -424,29 +392,44 @@ sfa_prefill_kernel(const PrefillArgs a) {
             issue_q(id2);
             issue(nx.kview, 0, kbuf(0));
             if (nx.n_kt > 1) issue(nx.kview, 1, kbuf(1));
-            if (j & 1) issue(nx.vview, 0, vbuf(0));
+            if (m & 1) issue(nx.vview, 0, vbuf(0));
         }
-
-        // this wave's last key tile holds its diagonal and needs the mask
+    };
+    auto phase_a = [&](int m, const Item& cur) {
+        const int last = cur.wave_kt - 1;      // the wave's diagonal tile takes the mask
+        if (m <= last) softmax(sc, m, m == last, cur.qi, pf);
+    };
+    // B(m) with m of parity PAR (fixes the LDS slots of K(m+1) and V(m))
+    auto phase_b = [&](auto par, int m, const Item& cur) {
+        constexpr int PAR = decltype(par)::value;
         const int last = cur.wave_kt - 1;
-        if (j < last) {
-            // hot path: S(j+1) = K(j+1) Q^T interleaved with the softmax of S(j)
-            bf16x8 pf[BN / 16];
-            qk(kbuf(j + 1), s_next);
-            softmax(s_cur, j, false, cur.qi, pf);
-            // 16 x {one K fragment read, one MFMA, a slice of softmax VALU}
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // VALU
+        f32x16(&S)[BN / 32] = sc;
+        f32x16(&O)[DBLK] = oacc;
+        const bf16x8(&Q)[DSTEPS] = qf;
+        const bf16x8(&P)[BN / 16] = pf;
+        if (m < last) {
+            if constexpr (D == 128) {
+                if constexpr (PAR == 0) asm volatile(HD_ASM_FULL_D128_P0 : HD_ASM_OUTS_FULL_D128 : HD_ASM_INS_FULL_D128 : HD_ASM_CLOBBERS);
+                else asm volatile(HD_ASM_FULL_D128_P1 : HD_ASM_OUTS_FULL_D128 : HD_ASM_INS_FULL_D128 : HD_ASM_CLOBBERS);
+            } else {
+                if constexpr (PAR == 0) asm volatile(HD_ASM_FULL_D64_P0 : HD_ASM_OUTS_FULL_D64 : HD_ASM_INS_FULL_D64 : HD_ASM_CLOBBERS);
+                else asm volatile(HD_ASM_FULL_D64_P1 : HD_ASM_OUTS_FULL_D64 : HD_ASM_INS_FULL_D64 : HD_ASM_CLOBBERS);
             }
-            pv(vbuf(j), pf);
-        } else if (j == last) {
-            bf16x8 pf[BN / 16];
-            softmax(s_cur, j, true, cur.qi, pf);
-            pv(vbuf(j), pf);
+        } else if (m == last) {
+            if constexpr (D == 128) {
+                if constexpr (PAR == 0) asm volatile(HD_ASM_PV_D128_P0 : HD_ASM_OUTS_PV_D128 : HD_ASM_INS_PV_D128 : HD_ASM_CLOBBERS);
+                else asm volatile(HD_ASM_PV_D128_P1 : HD_ASM_OUTS_PV_D128 : HD_ASM_INS_PV_D128 : HD_ASM_CLOBBERS);
+            } else {
+                if constexpr (PAR == 0) asm volatile(HD_ASM_PV_D64_P0 : HD_ASM_OUTS_PV_D64 : HD_ASM_INS_PV_D64 : HD_ASM_CLOBBERS);
+                else asm volatile(HD_ASM_PV_D64_P1 : HD_ASM_OUTS_PV_D64 : HD_ASM_INS_PV_D64 : HD_ASM_CLOBBERS);
+            }
         }
+    };
+    auto step = [&](auto par, int m, const Item& cur, uint32_t nid, bool more) {
+        if (wgrp) barrier_step(m, cur, nid, more);
+        phase_a(m, cur);
+        if (!wgrp) barrier_step(m, cur, nid, more);
+        phase_b(par, m, cur);
     };
 
     // ---- persistent loop over this workgroup's work items ----
@@ -471,16 +454,20 @@ sfa_prefill_kernel(const PrefillArgs a) {
         for (int i = 0; i < DBLK; ++i) oacc[i] = f32x16{};
         m_run = -INFINITY;
         l_run = 0.f;
-        f32x16 sa[BN / 32], sb[BN / 32];
-        if (cur.wave_kt > 0) qk(kbuf(0), sa);
-        for (int j = 0; j < cur.n_kt; j += 2) {
-            step(j, sa, sb, cur, nid, more);
-            if (j + 1 < cur.n_kt) step(j + 1, sb, sa, cur, nid, more);
+        if (cur.wave_kt > 0) {
+            f32x16(&S)[BN / 32] = sc;
+            const bf16x8(&Q)[DSTEPS] = qf;
+            if constexpr (D == 128) asm volatile(HD_ASM_QK_D128_P0 : HD_ASM_OUTS_QK_D128 : HD_ASM_INS_QK_D128 : HD_ASM_CLOBBERS);
+            else asm volatile(HD_ASM_QK_D64_P0 : HD_ASM_OUTS_QK_D64 : HD_ASM_INS_QK_D64 : HD_ASM_CLOBBERS);
+        }
+        for (int m = 0; m < cur.n_kt; m += 2) {
+            step(std::integral_constant<int, 0>{}, m, cur, nid, more);
+            if (m + 1 < cur.n_kt) step(std::integral_constant<int, 1>{}, m + 1, cur, nid, more);
         }
         // every wave has finished reading this item's tiles: the ring is free
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        // V(0) of the next item, unless the final step (odd F) already sent it
+        // V(0) of the next item, unless the final interval (odd F) already sent it
         if (more && (cur.n_kt & 1)) issue(make_item(nid).vview, 0, vbuf(0));
         store_out(cur.id, cur.qi);
         if (!more) break;
@@ -570,3 +557,4 @@ extern "C" hd_status sfa_mix_attn(const uint16_t* q, const uint16_t* k,
     return hdsfa::launch_prefill(q, k, v, out, B, n, L, Hq, Hkv, D, softmax_scale,
                                  stream, /*within=*/false);
 }
+
