@@ -98,7 +98,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-template <int D>
+// UNIT: softmax scale 1 (Q pre-scaled), so scale * log2(e) is a literal and the
+// exponent argument s * c - m takes the two-operand v_fmamk form
+template <int D, bool UNIT>
 __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 sfa_prefill_kernel(const PrefillArgs a) {
     constexpr int ROWB = D * 2;                // bytes per K/V row
@@ -317,7 +319,7 @@ sfa_prefill_kernel(const PrefillArgs a) {
         for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
             for (int it = 0; it < 16; ++it) mx = fmaxf(mx, sacc[kb][it]);
-        mx = halves_max(mx) * a.c;
+        mx = halves_max(mx) * (UNIT ? kLog2e : a.c);
         // Lazy rescale: the reference max m_run only moves when a row's tile
         // max exceeds it by more than 8 (a factor 2^8), so O and l are
         // rescaled rarely (always on the first tile).  Probabilities stay
@@ -331,11 +333,15 @@ sfa_prefill_kernel(const PrefillArgs a) {
             for (int i = 0; i < DBLK; ++i) oacc[i] *= alpha;
         }
         float rsp[4] = {0.f, 0.f, 0.f, 0.f};
+        // -m in a register of its own (not a negate modifier), so that with a
+        // literal scale the exponent argument is the two-operand v_fmamk_f32
+        float nm;
+        asm("v_xor_b32 %0, 0x80000000, %1" : "=v"(nm) : "v"(m_run));
 #pragma unroll
         for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
             for (int it = 0; it < 16; ++it) {
-                const float p = fast_exp2(__builtin_fmaf(sacc[kb][it], a.c, -m_run));
+                const float p = fast_exp2(__builtin_fmaf(sacc[kb][it], UNIT ? kLog2e : a.c, nm));
                 sacc[kb][it] = p;
                 rsp[it & 3] += p;
             }
@@ -531,9 +537,11 @@ hd_status launch_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v
     a.n_items = (uint32_t)items;
     const uint64_t blocks = items < (uint64_t)device_cus() ? items : (uint64_t)device_cus();
     if (D == 128)
-        sfa_prefill_kernel<128><<<dim3((uint32_t)blocks), dim3(THREADS), 0, stream>>>(a);
+        (scale == 1.f ? sfa_prefill_kernel<128, true> : sfa_prefill_kernel<128, false>)
+            <<<dim3((uint32_t)blocks), dim3(THREADS), 0, stream>>>(a);
     else
-        sfa_prefill_kernel<64><<<dim3((uint32_t)blocks), dim3(THREADS), 0, stream>>>(a);
+        (scale == 1.f ? sfa_prefill_kernel<64, true> : sfa_prefill_kernel<64, false>)
+            <<<dim3((uint32_t)blocks), dim3(THREADS), 0, stream>>>(a);
     return launch_status();
 }
 

@@ -130,6 +130,26 @@ def test_prefill_sweep(n, B, L, Hq, Hkv, D, mode):
     assert_close(f64(out), ref, f"sweep n={n} L={L} H={Hq}/{Hkv} D={D} mode={mode}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mode", [WITHIN, MIX])
+def test_prefill_nonunit_scale(D, mode):
+    """Unscaled Q with the softmax scale 1/sqrt(D) passed to the call: the
+    general-scale kernel (a scale of 1 takes a specialised one)."""
+    n, B, L, Hq, Hkv = 3, 1, 70, 8, 2
+    seed = 3100 + D + mode
+    N = n * L
+    q = _rand((B, N, Hq, D), 1.0, seed, "cpu")
+    k = _rand((B, N, Hkv, D), 1.0, seed + 1, "cpu")
+    v = _rand((B, N, Hkv, D), 1.0, seed + 2, "cpu")
+    scale = D ** -0.5
+    out = FNS[mode](q.to(DEV), k.to(DEV), v.to(DEV), n, scale)
+    ref = oracle.prefill_ref(si.bits(q), si.bits(k), si.bits(v), n, mode, scale)
+    assert_close(f64(out), ref, f"scale={scale:.4f} D={D} mode={mode}")
+    # the same product through the unit-scale kernel: Q pre-scaled on the host
+    out1 = FNS[mode]((q.float() * scale).to(torch.bfloat16).to(DEV), k.to(DEV), v.to(DEV), n, 1.0)
+    assert_close(f64(out1), ref, f"pre-scaled D={D} mode={mode}")
+
+
 def _sample_rows(N, n, count, seed):
     g = np.random.default_rng(seed)
     fixed = [0, 1, n - 1, n, 31, 32, 63, 64, 127, 128, N // 2, N - n - 1, N - 2, N - 1]
