@@ -344,7 +344,7 @@ def main():
             "head_dim": cfg.D, "useful_gflop_per_step": round(flops / 1e9, 3),
         },
         "roofline": {
-            "kernel": "sfa_prefill_kernel<128, true> (both layers; 2 launches per step)",
+            "kernel": "sfa_prefill_kernel<128, 2> (log2-unit scores; both layers, 2 launches per step)",
             "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
             "traffic": measured_traffic("sfa_prefill_kernel_n4", "prefill.hip"),

@@ -98,9 +98,17 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// UNIT: softmax scale 1 (Q pre-scaled), so scale * log2(e) is a literal and the
-// exponent argument s * c - m takes the two-operand v_fmamk form
-template <int D, bool UNIT>
+// Scale modes: the exponent argument of a score s is s * c - m with
+// c = softmax scale * log2(e).
+//   kScaleAny:  c from the arguments (v_fma_f32, 8-byte encoding);
+//   kScaleUnit: scale 1 (Q carries the softmax scale), c = log2(e) is a literal
+//               (v_fmamk_f32, 8 bytes);
+//   kScaleLog2: c == 1 (Q also carries log2(e): scores arrive in log2 units),
+//               the argument is s - m (v_add_f32, 4 bytes).
+// The softmax issue time of a wave is close to proportional to its
+// instruction bytes, so the shorter form matters.
+constexpr int kScaleAny = 0, kScaleUnit = 1, kScaleLog2 = 2;
+template <int D, int MODE>
 __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 sfa_prefill_kernel(const PrefillArgs a) {
     constexpr int ROWB = D * 2;                // bytes per K/V row
@@ -118,6 +126,14 @@ sfa_prefill_kernel(const PrefillArgs a) {
     const int wave = tid >> 6;
     const int l32 = lane & 31;
     const int hh = lane >> 5;                  // half-wave index
+    // the lane index through an opaque copy: address arithmetic derived from
+    // it in code that runs once per item is computed where it is used instead
+    // of being hoisted out of the key loop and held in registers
+    auto lane_here = [&]() __attribute__((always_inline)) -> uint32_t {
+        uint32_t v;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "v"((uint32_t)lane));
+        return v;
+    };
 
     const int qblocks = NW / a.P;
     const uint32_t BT = MQ * qblocks;          // query rows per work item
@@ -218,14 +234,15 @@ sfa_prefill_kernel(const PrefillArgs a) {
     // requested any time after that.
     unsigned char* const qlds = smem + 2 * NSTAGE * TILE_B + wave * QW_B;
     auto issue_q = [&](uint32_t id) {
+        const uint32_t ln = lane_here();
         uint32_t q0;
         const uint64_t hoff = item_head(id, q0);
         const char* src = reinterpret_cast<const char*>(
-            a.q + hoff + (uint64_t)min(q0 + l32, a.len - 1u) * a.q_row);
+            a.q + hoff + (uint64_t)min(q0 + (ln & 31u), a.len - 1u) * a.q_row);
 #pragma unroll
         for (int e = 0; e < DSTEPS; ++e)
             __builtin_amdgcn_global_load_lds(
-                (const void __attribute__((address_space(1)))*)(src + (2 * e + hh) * 16),
+                (const void __attribute__((address_space(1)))*)(src + (2 * e + (ln >> 5)) * 16),
                 (void __attribute__((address_space(3)))*)(qlds + e * 1024), 16, 0, 0);
     };
 
@@ -236,20 +253,21 @@ sfa_prefill_kernel(const PrefillArgs a) {
     // (16-byte chunks XOR-swizzled by row), reads them back 4 lanes per row,
     // and stores whole 64-byte row pieces.
     auto store_out = [&](uint32_t id, uint32_t qi) {
+        const uint32_t ln = lane_here(), r32 = ln & 31u, h2 = ln >> 5;
         uint32_t q0;
         uint16_t* obase = a.o + item_head(id, q0);
         const float inv = 1.f / l_run;         // unused (never stored) where qi >= len
         if constexpr (TILE_B >= NW * 2048) {
             unsigned char* stg = vbuf(1) + wave * 2048;
-            const uint32_t rr = (uint32_t)lane >> 2, rc = (uint32_t)lane & 3u;
+            const uint32_t rr = ln >> 2, rc = ln & 3u;
 #pragma unroll
             for (int db = 0; db < DBLK; ++db) {
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const u32x2 w = {pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv),
                                      pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
-                    const uint32_t pc = (uint32_t)g ^ (((uint32_t)l32 >> 2) & 3u);
-                    *reinterpret_cast<u32x2*>(stg + l32 * 64 + pc * 16 + hh * 8) = w;
+                    const uint32_t pc = (uint32_t)g ^ ((r32 >> 2) & 3u);
+                    *reinterpret_cast<u32x2*>(stg + r32 * 64 + pc * 16 + h2 * 8) = w;
                 }
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
@@ -266,7 +284,7 @@ sfa_prefill_kernel(const PrefillArgs a) {
             for (int db = 0; db < DBLK; ++db)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const int d = db * 32 + 8 * g + 4 * hh;
+                    const int d = db * 32 + 8 * g + 4 * (int)h2;
                     u32x2 w = {pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv),
                                pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
                     *reinterpret_cast<u32x2*>(orow + d) = w;
@@ -303,6 +321,17 @@ sfa_prefill_kernel(const PrefillArgs a) {
 
     // online softmax of one tile's scores; returns the P^T operands.  The
     // causal mask is needed only on a wave's last (diagonal) tile.
+    //
+    // Lazy rescale: the reference max m_run only moves when a row's tile max
+    // exceeds it by more than 8 (a factor 2^8), so O and l are rescaled
+    // rarely (always on the first tile).  Probabilities stay <= 2^8 and the
+    // result O / l is unchanged.  Away from the first and the diagonal tile
+    // the tile max is not computed at all: the exponentials are taken with the
+    // current m_run, and if no row's tile sum exceeds 2^8 then no p exceeds
+    // 2^8, so no row's max exceeds m_run + 8 and the max test would not have
+    // rescaled either.  Only when a row's sum exceeds 2^8 (rare once the max
+    // has settled) are the max test and the exponentials done again, which
+    // gives exactly the result of always testing the max.
     auto softmax = [&](f32x16 (&sacc)[BN / 32], int kt, bool diag, uint32_t qi, bf16x8 (&pf)[BN / 16]) {
         if (diag) {
             const uint32_t k0 = (uint32_t)kt * BN;
@@ -314,46 +343,61 @@ sfa_prefill_kernel(const PrefillArgs a) {
                     if (key > qi) sacc[kb][it] = -INFINITY;
                 }
         }
-        float mx = -INFINITY;
+        auto max_test = [&]() __attribute__((always_inline)) {
+            float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb)
+            for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-            for (int it = 0; it < 16; ++it) mx = fmaxf(mx, sacc[kb][it]);
-        mx = halves_max(mx) * (UNIT ? kLog2e : a.c);
-        // Lazy rescale: the reference max m_run only moves when a row's tile
-        // max exceeds it by more than 8 (a factor 2^8), so O and l are
-        // rescaled rarely (always on the first tile).  Probabilities stay
-        // <= 2^8 and the result O / l is unchanged.
-        if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.f) != 0) {
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = fast_exp2(m_run - m_new);
-            m_run = m_new;
-            l_run *= alpha;
+                for (int it = 0; it < 16; ++it) mx = fmaxf(mx, sacc[kb][it]);
+            if constexpr (MODE == kScaleUnit) mx = halves_max(mx) * kLog2e;
+            else if constexpr (MODE == kScaleAny) mx = halves_max(mx) * a.c;
+            else mx = halves_max(mx);
+            if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.f) != 0) {
+                const float m_new = fmaxf(m_run, mx);
+                const float alpha = fast_exp2(m_run - m_new);
+                m_run = m_new;
+                l_run *= alpha;
 #pragma unroll
-            for (int i = 0; i < DBLK; ++i) oacc[i] *= alpha;
-        }
-        float rsp[4] = {0.f, 0.f, 0.f, 0.f};
-        // -m in a register of its own (not a negate modifier), so that with a
-        // literal scale the exponent argument is the two-operand v_fmamk_f32
-        float nm;
-        asm("v_xor_b32 %0, 0x80000000, %1" : "=v"(nm) : "v"(m_run));
-#pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-            for (int it = 0; it < 16; ++it) {
-                const float p = fast_exp2(__builtin_fmaf(sacc[kb][it], UNIT ? kLog2e : a.c, nm));
-                sacc[kb][it] = p;
-                rsp[it & 3] += p;
+                for (int i = 0; i < DBLK; ++i) oacc[i] *= alpha;
             }
-        l_run += halves_sum((rsp[0] + rsp[1]) + (rsp[2] + rsp[3]));
-        // P^T fragments (B operand): 16-key step c takes items 8*(c%2)..+7
+        };
+        // p = 2^(s*c - m_run) into the P^T fragments (16-key step c takes
+        // items 8*(c%2)..+7); returns the row's tile sum.  S is left intact.
+        auto exps = [&]() __attribute__((always_inline)) -> float {
+            // -m in a register of its own (not a negate modifier), so that the
+            // exponent argument has a two-operand form (v_fmamk_f32 / v_add_f32)
+            float nm;
+            asm("v_xor_b32 %0, 0x80000000, %1" : "=v"(nm) : "v"(m_run));
+            float rsp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < BN / 16; ++c) {
-            const f32x16& s = sacc[c >> 1];
-            const int o8 = (c & 1) * 8;
-            pf[c] = to_bf16x8(f32x8{s[o8 + 0], s[o8 + 1], s[o8 + 2], s[o8 + 3],
-                                    s[o8 + 4], s[o8 + 5], s[o8 + 6], s[o8 + 7]});
+            for (int c = 0; c < BN / 16; ++c) {
+                const f32x16& sv = sacc[c >> 1];
+                const int o8 = (c & 1) * 8;
+                f32x8 pv;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    float x;
+                    if constexpr (MODE == kScaleLog2) x = sv[o8 + j] + nm;
+                    else x = __builtin_fmaf(sv[o8 + j], MODE == kScaleUnit ? kLog2e : a.c, nm);
+                    pv[j] = fast_exp2(x);
+                    rsp[j & 3] += pv[j];
+                }
+                pf[c] = to_bf16x8(pv);
+            }
+            return halves_sum((rsp[0] + rsp[1]) + (rsp[2] + rsp[3]));
+        };
+        float ts;
+        if (diag || kt == 0) {
+            max_test();
+            ts = exps();
+        } else {
+            ts = exps();
+            if (__builtin_amdgcn_ballot_w64(ts > 256.f) != 0) {
+                max_test();
+                ts = exps();
+            }
         }
+        l_run += ts;
     };
 
     // ---- software pipeline over key tiles ----
@@ -536,12 +580,13 @@ hd_status launch_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v
     if (items > 0x7fffffffULL) return HD_ERR_UNSUPPORTED;
     a.n_items = (uint32_t)items;
     const uint64_t blocks = items < (uint64_t)device_cus() ? items : (uint64_t)device_cus();
-    if (D == 128)
-        (scale == 1.f ? sfa_prefill_kernel<128, true> : sfa_prefill_kernel<128, false>)
-            <<<dim3((uint32_t)blocks), dim3(THREADS), 0, stream>>>(a);
-    else
-        (scale == 1.f ? sfa_prefill_kernel<64, true> : sfa_prefill_kernel<64, false>)
-            <<<dim3((uint32_t)blocks), dim3(THREADS), 0, stream>>>(a);
+    const int mode = a.c == 1.f ? kScaleLog2 : (scale == 1.f ? kScaleUnit : kScaleAny);
+    auto kern = D == 128
+        ? (mode == kScaleLog2 ? sfa_prefill_kernel<128, kScaleLog2>
+           : mode == kScaleUnit ? sfa_prefill_kernel<128, kScaleUnit> : sfa_prefill_kernel<128, kScaleAny>)
+        : (mode == kScaleLog2 ? sfa_prefill_kernel<64, kScaleLog2>
+           : mode == kScaleUnit ? sfa_prefill_kernel<64, kScaleUnit> : sfa_prefill_kernel<64, kScaleAny>);
+    kern<<<dim3((uint32_t)blocks), dim3(THREADS), 0, stream>>>(a);
     return launch_status();
 }
 

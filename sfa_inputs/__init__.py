@@ -8,8 +8,12 @@ bits produced here.
 Workloads (all synthetic, seeded):
   tiny    n=2, B=1, L=64, 2/2 heads, D=64, Q/K/V ~ N(0,1)/8, scale 1;
           expansion vocab 1000, hidden 128, tables ~ N(0, 0.02)
-  n4      n=4, B=2, L=1024, 32/8 heads, D=128, Q ~ N(0,1)/sqrt(128),
-          K, V ~ N(0,1), scale 1; expansion vocab 151936, hidden 4096
+  n4      n=4, B=2, L=1024, 32/8 heads, D=128, Q ~ N(0,1) * log2(e)/sqrt(128),
+          K, V ~ N(0,1), scale ln 2; expansion vocab 151936, hidden 4096.
+          Q carries the softmax scale 1/sqrt(128) and the factor log2(e),
+          so scale * q.k * log2(e) = q.k / sqrt(128) in natural units: the
+          scores have the distribution of unscaled N(0,1) Q with scale
+          1/sqrt(128), and the kernel receives them in log2 units
   n8stack n=8, B=1, L=2048, 32/8 heads, D=128, pre-scaled as n4; a stack of
           three within-stream layers and one mixing layer
   long    n=4, B=1, L=8192, 64/4 heads, D=128, pre-scaled as n4
@@ -75,14 +79,16 @@ class DecodeCfg:
 TINY = PrefillCfg("tiny", 1, n=2, B=1, L=64, Hq=2, Hkv=2, D=64, q_std=1 / 8,
                   kv_std=1 / 8, scale=1.0, vocab=1000, hidden=128,
                   layers=("within", "mix"))
+LOG2E = math.log2(math.e)
+LN2 = math.log(2.0)
 N4 = PrefillCfg("n4", 2, n=4, B=2, L=1024, Hq=32, Hkv=8, D=128,
-                q_std=1 / math.sqrt(128), kv_std=1.0, scale=1.0, vocab=151936,
+                q_std=LOG2E / math.sqrt(128), kv_std=1.0, scale=LN2, vocab=151936,
                 hidden=4096, layers=("within", "mix"))
 N8STACK = PrefillCfg("n8stack", 3, n=8, B=1, L=2048, Hq=32, Hkv=8, D=128,
-                     q_std=1 / math.sqrt(128), kv_std=1.0, scale=1.0,
+                     q_std=LOG2E / math.sqrt(128), kv_std=1.0, scale=LN2,
                      layers=("within", "within", "within", "mix"))
 LONG = PrefillCfg("long", 4, n=4, B=1, L=8192, Hq=64, Hkv=4, D=128,
-                  q_std=1 / math.sqrt(128), kv_std=1.0, scale=1.0,
+                  q_std=LOG2E / math.sqrt(128), kv_std=1.0, scale=LN2,
                   layers=("within", "mix"))
 DECODE = DecodeCfg("decode", 5, S=64, n=4, T=4096, Hq=32, Hkv=8, D=128,
                    scale=1 / math.sqrt(128))

@@ -134,7 +134,9 @@ def test_prefill_sweep(n, B, L, Hq, Hkv, D, mode):
 @pytest.mark.parametrize("mode", [WITHIN, MIX])
 def test_prefill_nonunit_scale(D, mode):
     """Unscaled Q with the softmax scale 1/sqrt(D) passed to the call: the
-    general-scale kernel (a scale of 1 takes a specialised one)."""
+    general-scale kernel.  The same product through the two specialised ones:
+    scale 1 (Q carries the scale) and scale ln 2 (Q also carries log2(e), so
+    scale * log2(e) == 1 in float32)."""
     n, B, L, Hq, Hkv = 3, 1, 70, 8, 2
     seed = 3100 + D + mode
     N = n * L
@@ -148,6 +150,10 @@ def test_prefill_nonunit_scale(D, mode):
     # the same product through the unit-scale kernel: Q pre-scaled on the host
     out1 = FNS[mode]((q.float() * scale).to(torch.bfloat16).to(DEV), k.to(DEV), v.to(DEV), n, 1.0)
     assert_close(f64(out1), ref, f"pre-scaled D={D} mode={mode}")
+    # and with log2(e) folded in as well: scores arrive in log2 units
+    out2 = FNS[mode]((q.float() * (scale * si.LOG2E)).to(torch.bfloat16).to(DEV), k.to(DEV), v.to(DEV),
+                     n, si.LN2)
+    assert_close(f64(out2), ref, f"log2 units D={D} mode={mode}")
 
 
 def _sample_rows(N, n, count, seed):
