@@ -24,8 +24,27 @@ def sees(t, s, t2, s2, within):
     return t2 < t or (t2 == t and s2 <= s)
 
 
-def brute_attention(q, k, v, n, within, scale):
+def window_members(t, s, n, window):
+    """The (token, stream) pairs inside a sliding window of ``window``
+    positions ending at (t, s), found by walking back through the interleaved
+    order one position at a time (stream s, s-1, ..., 0, then the previous
+    token's stream n-1, ...).  Review, *Method*: mixing layers follow the base
+    model's sliding-window pattern over the expanded sequence."""
+    out = set()
+    tt, ss = t, s
+    for _ in range(window):
+        if tt < 0:
+            break
+        out.add((tt, ss))
+        ss -= 1
+        if ss < 0:
+            tt, ss = tt - 1, n - 1
+    return out
+
+
+def brute_attention(q, k, v, n, within, scale, window=None):
     """q[b][p][h][d], k/v[b][p][g][d] as nested Python float lists, p = t*n+s.
+    ``window`` (mixing only): sliding window in positions.
     Returns out[b][p][h][d]."""
     B = len(q)
     N = len(q[0])
@@ -40,6 +59,7 @@ def brute_attention(q, k, v, n, within, scale):
         for t in range(L):
             for s in range(n):
                 p = t * n + s
+                inside = None if window is None else window_members(t, s, n, window)
                 oh = []
                 for h in range(Hq):
                     g = h // G
@@ -48,6 +68,8 @@ def brute_attention(q, k, v, n, within, scale):
                     for t2 in range(L):
                         for s2 in range(n):
                             if not sees(t, s, t2, s2, within):
+                                continue
+                            if inside is not None and (t2, s2) not in inside:
                                 continue
                             p2 = t2 * n + s2
                             dot = 0.0

@@ -27,7 +27,11 @@ Readings where the pages are silent (each listed in the design notes):
      interleaved order);
   R5 the softmax scale is an explicit argument;
   R6 query head h reads KV head h // (Hq / Hkv);
-  R7 an out-of-range token id yields an all-zero row and raises a flag.
+  R7 an out-of-range token id yields an all-zero row and raises a flag;
+  R13 a sliding-window mixing layer (review, *Method*: the mixing layers
+     follow the base model's own pattern, sliding-window or full) has a window
+     W counted in positions of the interleaved order: position i sees
+     i - W < j <= i (the pages give no W; a base window of w tokens is W = n*w).
 
 No function here is "parity unpinned": every one is pinned in
 ``tests/test_oracle.py`` against brute force, a library routine, a closed form
@@ -38,7 +42,7 @@ from __future__ import annotations
 import numpy as np
 
 WITHIN = 0  # within-stream layer
-MIX = 1     # mixing layer, full causal over the interleaved order
+MIX = 1     # mixing layer, causal over the interleaved order (full, or with a window)
 
 
 # ---------------------------------------------------------------------------
@@ -115,7 +119,7 @@ def cyclic_replicate_ref(tables, n_new):
 # ---------------------------------------------------------------------------
 # (2) The SFA visibility rule
 # ---------------------------------------------------------------------------
-def visible(i, j, n, mode):
+def visible(i, j, n, mode, window=None):
     """True where key position j is visible to query position i.
 
     Within-stream (review, *Method*: "attend only within their own stream"):
@@ -123,6 +127,8 @@ def visible(i, j, n, mode):
         (reading R3, so a query sees itself).
     Mixing, full pattern (review, *Method*: the base model's own full causal
         pattern, here over the interleaved order, reading R4): j <= i.
+    Mixing, sliding-window pattern (same passage; reading R13): additionally
+        j > i - window.
 
     Works elementwise on NumPy integer arrays (broadcasting).
     """
@@ -130,21 +136,28 @@ def visible(i, j, n, mode):
     j = np.asarray(j)
     causal = j <= i
     if mode == WITHIN:
+        if window is not None:
+            raise ValueError("a window applies to mixing layers only")
         return causal & ((j % n) == (i % n))
     if mode == MIX:
-        return causal
+        if window is None:
+            return causal
+        if window < 1:
+            raise ValueError("window must be >= 1")
+        return causal & (j > i - window)
     raise ValueError(f"unknown mode {mode}")
 
 
-def count_pairs(N, n, mode):
+def count_pairs(N, n, mode, window=None):
     """Number of visible (query, key) pairs in one (batch, head) of length N,
     counted by enumerating the visibility rule (used to check the closed forms
-    n*L*(L+1)/2 and N*(N+1)/2 and the review's O(nL^2) vs O(n^2 L^2) orders)."""
+    n*L*(L+1)/2, N*(N+1)/2 and, with a window W <= N, W(W+1)/2 + (N-W)W, and
+    the review's O(nL^2) vs O(n^2 L^2) orders)."""
     j = np.arange(N)[None, :]
     total = 0
     for r0 in range(0, N, 1024):
         i = np.arange(r0, min(N, r0 + 1024))[:, None]
-        total += int(np.count_nonzero(visible(i, j, n, mode)))
+        total += int(np.count_nonzero(visible(i, j, n, mode, window)))
     return total
 
 
@@ -159,7 +172,7 @@ def _softmax_rows(scores):
     return p / p.sum(axis=1, keepdims=True)
 
 
-def attention_rows(q_rows, q_pos, k, v, n, mode, scale):
+def attention_rows(q_rows, q_pos, k, v, n, mode, scale, window=None):
     """softmax(scale * q k^T + mask) v for some query rows of one head.
 
     q_rows : float64 [R, D]   the queries
@@ -168,7 +181,7 @@ def attention_rows(q_rows, q_pos, k, v, n, mode, scale):
     returns (out [R, D], probs [R, Nk]) in float64.
     """
     j = np.arange(k.shape[0])[None, :]
-    mask = visible(np.asarray(q_pos)[:, None], j, n, mode)
+    mask = visible(np.asarray(q_pos)[:, None], j, n, mode, window)
     scores = scale * (q_rows @ k.T)
     scores = np.where(mask, scores, -np.inf)
     probs = _softmax_rows(scores)
@@ -176,12 +189,13 @@ def attention_rows(q_rows, q_pos, k, v, n, mode, scale):
 
 
 def prefill_ref(q, k, v, n, mode, scale, rows=None, heads=None, batches=None,
-                chunk=1024):
+                chunk=1024, window=None):
     """Prefill SFA layer (review, *Method*; abstract; README *Key Idea*).
 
     q      : bf16 bits [B, N, Hq, D]; k, v : bf16 bits [B, N, Hkv, D];
              N = n*L in the interleaved order (reading R1)
     mode   : WITHIN or MIX
+    window : MIX only: sliding window W (reading R13); None = full pattern
     rows   : optional int array of query positions to compute (default all)
     heads  : optional query heads (default all); batches likewise
     returns float64 [len(batches), len(rows), len(heads), D]
@@ -212,7 +226,7 @@ def prefill_ref(q, k, v, n, mode, scale, rows=None, heads=None, batches=None,
                 # keys later than the last requested row are never visible
                 nk = int(r.max()) + 1
                 qf = bf16_bits_to_f64(q[b, r, h, :])
-                o, _ = attention_rows(qf, r, kf[:nk], vf[:nk], n, mode, scale)
+                o, _ = attention_rows(qf, r, kf[:nk], vf[:nk], n, mode, scale, window)
                 out[bi, c0:c0 + len(r), hi, :] = o
     return out
 
@@ -273,9 +287,9 @@ def decode_ref(q_new, k_cache, v_cache, tokens_before, n, mode, scale,
 # ---------------------------------------------------------------------------
 # (5) Useful work (closed forms checked against count_pairs in the tests)
 # ---------------------------------------------------------------------------
-def useful_flops(B, n, L, Hq, D, mode):
+def useful_flops(B, n, L, Hq, D, mode, window=None):
     """4*D FLOPs per visible (query, key) pair per query head: 2*D for the
     score, 2*D for the value accumulation."""
     N = n * L
-    pairs = count_pairs(N, n, mode)
+    pairs = count_pairs(N, n, mode, window)
     return 4 * D * Hq * B * pairs

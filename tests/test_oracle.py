@@ -188,6 +188,74 @@ def test_prefill_matches_brute_force(n, L, Hq, Hkv, D, mode):
     np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
 
 
+# ---------------------------------------------------------------------------
+# sliding-window mixing (reading R13)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("N,W", [(1, 1), (17, 1), (17, 5), (64, 64), (64, 100), (130, 64),
+                                 (4096, 1024)])
+def test_window_pair_count_closed_form(N, W):
+    """Row i sees min(i+1, W) keys: W(W+1)/2 + (N-W)W pairs when W <= N."""
+    want = W * (W + 1) // 2 + (N - W) * W if W <= N else N * (N + 1) // 2
+    assert oracle.count_pairs(N, 4, MIX, window=W) == want
+
+
+def test_window_one_is_identity():
+    """W = 1: each position sees only itself, so the output is its own v."""
+    rng = np.random.default_rng(31)
+    q, k, v = _qkv(rng, 2, 3, 11, 4, 2, 16)
+    got = oracle.prefill_ref(q, k, v, 3, MIX, 0.9, window=1)
+    vf = _f(v)
+    want = np.repeat(vf, 2, axis=2)            # query head h reads KV head h // 2
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-15)
+
+
+def test_window_two_is_a_logistic_blend():
+    """W = 2: position i > 0 blends v_{i-1} and v_i with weights sigma(a) and
+    sigma(-a), a = scale * q_i . (k_{i-1} - k_i); position 0 returns v_0."""
+    rng = np.random.default_rng(32)
+    n, L, scale = 2, 9, 0.6
+    q, k, v = _qkv(rng, 1, n, L, 2, 1, 8)
+    got = oracle.prefill_ref(q, k, v, n, MIX, scale, window=2)
+    qf, kf, vf = _f(q)[0], _f(k)[0, :, 0], _f(v)[0, :, 0]
+    for i in range(n * L):
+        for h in range(2):
+            if i == 0:
+                want = vf[0]
+            else:
+                a = scale * float(qf[i, h] @ (kf[i - 1] - kf[i]))
+                w = 1.0 / (1.0 + math.exp(-a))
+                want = w * vf[i - 1] + (1.0 - w) * vf[i]
+            np.testing.assert_allclose(got[0, i, h], want, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("n,L,W", [(1, 20, 3), (2, 12, 1), (2, 12, 5), (3, 8, 7), (4, 6, 24),
+                                   (4, 6, 40)])
+def test_window_matches_brute_force(n, L, W):
+    rng = np.random.default_rng(500 + W + n)
+    q, k, v = _qkv(rng, 1, n, L, 4, 2, 8)
+    got = oracle.prefill_ref(q, k, v, n, MIX, 0.8, window=W)
+    ref = np.array(brute.brute_attention(_f(q).tolist(), _f(k).tolist(), _f(v).tolist(),
+                                         n, False, 0.8, window=W))
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_window_planted_off_by_one_is_caught(monkeypatch):
+    real = sfa.visible
+
+    def wide(i, j, n, mode, window=None):     # j >= i - W: one key too many
+        if window is None:
+            return real(i, j, n, mode)
+        return real(i, j, n, mode) | ((np.asarray(j) <= np.asarray(i)) &
+                                       (np.asarray(j) == np.asarray(i) - window))
+
+    monkeypatch.setattr(sfa, "visible", wide)
+    with pytest.raises(AssertionError):
+        test_window_one_is_identity()
+    with pytest.raises(AssertionError):
+        test_window_pair_count_closed_form(17, 5)
+    monkeypatch.setattr(sfa, "visible", real)
+
+
 @pytest.mark.parametrize("mode", [WITHIN, MIX])
 def test_n1_is_ordinary_causal_attention(mode):
     rng = np.random.default_rng(7)
@@ -401,19 +469,19 @@ def test_planted_mistakes_are_caught(monkeypatch):
     assert _pins_pass()
     real = sfa.visible
 
-    def strict(i, j, n, mode):         # forgets the query's own position
-        return real(i, j, n, mode) & (np.asarray(j) != np.asarray(i))
+    def strict(i, j, n, mode, window=None):         # forgets the query's own position
+        return real(i, j, n, mode, window) & (np.asarray(j) != np.asarray(i))
 
-    def no_stream(i, j, n, mode):      # within-stream without the stream test
+    def no_stream(i, j, n, mode, window=None):      # within-stream without the stream test
         return np.asarray(j) <= np.asarray(i)
 
-    def token_stream(i, j, n, mode):   # stream taken as i // n
+    def token_stream(i, j, n, mode, window=None):   # stream taken as i // n
         i, j = np.asarray(i), np.asarray(j)
         c = j <= i
         return c & ((j // n) == (i // n)) if mode == WITHIN else c
 
-    def anti(i, j, n, mode):           # causality reversed
-        return real(j, i, n, mode)
+    def anti(i, j, n, mode, window=None):           # causality reversed
+        return real(j, i, n, mode, window)
 
     for bad in (strict, no_stream, token_stream, anti):
         monkeypatch.setattr(sfa, "visible", bad)
