@@ -36,15 +36,23 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
 
-def pairs(n, L, mode):
+WINDOW = 1024                 # sliding window measured (positions; 256 tokens at n=4)
+
+
+def pairs(n, L, mode, window=None):
     """Visible (query, key) pairs per (batch, head): n*L*(L+1)/2 within-stream,
-    N*(N+1)/2 mixing (N = n*L)."""
+    N*(N+1)/2 mixing (N = n*L); with a sliding window W < N, row i sees
+    min(i+1, W) keys: W*(W+1)/2 + (N-W)*W."""
     N = n * L
-    return n * L * (L + 1) // 2 if mode == "within" else N * (N + 1) // 2
+    if mode == "within":
+        return n * L * (L + 1) // 2
+    if window is not None and window < N:
+        return window * (window + 1) // 2 + (N - window) * window
+    return N * (N + 1) // 2
 
 
-def attn_flops(B, n, L, Hq, D, mode):
-    return 4 * D * Hq * B * pairs(n, L, mode)
+def attn_flops(B, n, L, Hq, D, mode, window=None):
+    return 4 * D * Hq * B * pairs(n, L, mode, window)
 
 
 def decode_bytes(S, n, T, Hkv, D):
@@ -119,12 +127,23 @@ def bench_prefill(args, torch, hd, si):
     t_exp = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     t_w = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     t_m = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    # the sliding-window mixing layer (not part of the step): same inputs
+    for _ in range(3):
+        hd.mix_attn_window(q, k, v, cfg.n, cfg.scale, WINDOW, out=om)
+    ew = _events(2)
+    ew[0].record()
+    for _ in range(args.steps):
+        hd.mix_attn_window(q, k, v, cfg.n, cfg.scale, WINDOW, out=om)
+    ew[1].record()
+    torch.cuda.synchronize()
+    t_mw = ew[0].elapsed_time(ew[1]) / args.steps
 
     fw = attn_flops(cfg.B, cfg.n, cfg.L, cfg.Hq, cfg.D, "within")
     fm = attn_flops(cfg.B, cfg.n, cfg.L, cfg.Hq, cfg.D, "mix")
+    fmw = attn_flops(cfg.B, cfg.n, cfg.L, cfg.Hq, cfg.D, "mix", WINDOW)
     exp_bytes = cfg.B * cfg.N * cfg.hidden * 2 * 2 + cfg.B * cfg.L * 4
     res = dict(cfg=cfg, ms_step=ms_step, t_exp=t_exp, t_w=t_w, t_m=t_m, fw=fw, fm=fm,
-               exp_bytes=exp_bytes)
+               exp_bytes=exp_bytes, t_mw=t_mw, fmw=fmw)
     del ids, tab, q, k, v, x, ow, om
     torch.cuda.empty_cache()
     return res
@@ -320,6 +339,12 @@ def main():
         "sfa_mix_attn": {"ms": round(pf["t_m"], 4), "bound": "mfma",
                          "achieved": round(pf["fm"] / (pf["t_m"] * 1e-3) / 1e12, 2),
                          "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS},
+        "sfa_mix_attn_window": {"ms": round(pf["t_mw"], 4), "bound": "mfma",
+                                "achieved": round(pf["fmw"] / (pf["t_mw"] * 1e-3) / 1e12, 2),
+                                "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS,
+                                "window": WINDOW, "useful_gflop": round(pf["fmw"] / 1e9, 3),
+                                "note": "sliding-window mixing layer, same n4 inputs; "
+                                        "not part of the step"},
     }
     for kk in kernels.values():
         kk["frac"] = round(kk["achieved"] / kk["peak"], 4)

@@ -117,6 +117,26 @@ hd_status sfa_mix_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        hipStream_t stream);
 
 /*
+ * sfa_mix_attn_window -- mixing attention with the sliding-window pattern
+ * (prefill).  Review, section Method: the mixing layers follow the base
+ * model's own attention pattern, sliding-window or full (the 80B model has 23
+ * sliding-window mixing layers of 49).  The pages give no window size; here
+ * the window W is counted in positions of the interleaved length-nL order
+ * (a base-model window of w tokens is W = n*w):
+ *
+ *   O[b, i, h] = sum over i - W < j <= i of softmax_j(scale * q[b,i,h] . k[b,j,g]) v[b,j,g]
+ *
+ *   window   W >= 1; W >= nL gives exactly sfa_mix_attn
+ *
+ * Same arguments, layouts, precision and errors as sfa_stream_attn, plus
+ * HD_ERR_SHAPE for window < 1.
+ */
+hd_status sfa_mix_attn_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              uint16_t* out, int64_t B, int32_t n, int64_t L,
+                              int32_t Hq, int32_t Hkv, int32_t D, float softmax_scale,
+                              int64_t window, hipStream_t stream);
+
+/*
  * sfa_decode_workspace_size -- bytes of device workspace sfa_decode_step
  * needs for these sizes (fp32 split partials).  Returns 0 for invalid sizes.
  */

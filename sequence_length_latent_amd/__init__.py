@@ -15,8 +15,8 @@ import torch
 
 from ._lib import HDError, check, load  # noqa: F401
 
-__all__ = ["expand", "stream_attn", "mix_attn", "decode_workspace_size", "decode_step",
-           "HDError", "load", "WITHIN", "MIX"]
+__all__ = ["expand", "stream_attn", "mix_attn", "mix_attn_window", "decode_workspace_size",
+           "decode_step", "HDError", "load", "WITHIN", "MIX"]
 
 WITHIN = 0
 MIX = 1
@@ -63,7 +63,7 @@ def expand(ids: torch.Tensor, tables: torch.Tensor, out: torch.Tensor | None = N
     return out
 
 
-def _attn(fn_name: str, q, k, v, n: int, scale: float, out):
+def _attn(fn_name: str, q, k, v, n: int, scale: float, out, window=None):
     _need(q, "q", torch.bfloat16, 4)
     _need(k, "k", torch.bfloat16, 4)
     _need(v, "v", torch.bfloat16, 4)
@@ -78,8 +78,9 @@ def _attn(fn_name: str, q, k, v, n: int, scale: float, out):
     _need(out, "out", torch.bfloat16, 4)
     if out.shape != q.shape:
         raise ValueError("out must match q")
+    extra = () if window is None else (int(window),)
     st = getattr(load(), fn_name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                  B, n, N // n, Hq, Hkv, D, float(scale), _stream())
+                                  B, n, N // n, Hq, Hkv, D, float(scale), *extra, _stream())
     check(fn_name, st)
     return out
 
@@ -92,6 +93,12 @@ def stream_attn(q, k, v, n: int, scale: float, out=None):
 def mix_attn(q, k, v, n: int, scale: float, out=None):
     """Mixing attention: full causal over the interleaved n*L order."""
     return _attn("sfa_mix_attn", q, k, v, n, scale, out)
+
+
+def mix_attn_window(q, k, v, n: int, scale: float, window: int, out=None):
+    """Mixing attention, sliding-window pattern: position i sees keys j with
+    i - window < j <= i in the interleaved n*L order (window >= 1)."""
+    return _attn("sfa_mix_attn_window", q, k, v, n, scale, out, window)
 
 
 def decode_workspace_size(S: int, n: int, Hq: int, Hkv: int, D: int, max_tokens: int) -> int:

@@ -15,6 +15,12 @@
 // key tiles of its own stream that are not in its future: nothing is computed
 // for the (n-1)/n of pairs the mask removes.
 //
+// A sliding-window mixing layer (the base model's windowed pattern) is the
+// mixing view with a lower bound: query i sees keys j with i - W < j <= i
+// (W in expanded positions).  An item then starts at the key tile holding its
+// first row's oldest visible key, and the rows' lower bounds are masked on the
+// one or two tiles they cross.
+//
 // Work items are (query tile, batch, view, KV head, head pack), listed longest
 // causal extent first.  The grid is persistent, one workgroup per compute
 // unit: workgroup b takes item r*grid + b on even rounds r and
@@ -77,6 +83,7 @@ struct PrefillArgs {
     uint32_t n_hpacks;   // G / P
     uint32_t n_qtiles;   // ceil(len / (MQ * NW / P))
     uint32_t n_items;    // n_qtiles * B * groups * Hkv * n_hpacks
+    uint32_t window;     // sliding window W in rows of the view (WIN kernels only)
     float c;             // softmax scale * log2(e)
 };
 
@@ -108,7 +115,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // The softmax issue time of a wave is close to proportional to its
 // instruction bytes, so the shorter form matters.
 constexpr int kScaleAny = 0, kScaleUnit = 1, kScaleLog2 = 2;
-template <int D, int MODE>
+// WIN: sliding window (a.window < len); otherwise plain causal.
+template <int D, int MODE, bool WIN>
 __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 sfa_prefill_kernel(const PrefillArgs a) {
     constexpr int ROWB = D * 2;                // bytes per K/V row
@@ -151,8 +159,11 @@ sfa_prefill_kernel(const PrefillArgs a) {
         uint32_t id;
         const char* kview;
         const char* vview;
-        int n_kt;             // key tiles the workgroup visits
-        int wave_kt;          // key tiles this wave needs
+        int n_kt;             // key tiles up to the item's last (absolute end)
+        int wave_kt;          // key tiles this wave needs (absolute end)
+        int m_lo;             // first key tile of the item (0 without a window)
+        int wave_lo;          // this wave's first key tile
+        int lo_end;           // last tile holding a key below some row's window (-1: none)
         uint32_t qi;          // this lane's query row in the view
     };
     // (batch, view, query head) offset of an item, in elements, and its first row
@@ -186,8 +197,22 @@ sfa_prefill_kernel(const PrefillArgs a) {
         const uint32_t wave_end = min(a.len, q0 + MQ);       // exclusive
         it.wave_kt = q0 < a.len ? (int)((wave_end + BN - 1) / BN) : 0;
         it.qi = q0 + l32;
+        if constexpr (WIN) {
+            // oldest visible key of row r: r - W + 1 (clamped at 0)
+            const uint32_t f0 = qtile * BT;
+            it.m_lo = (int)((f0 >= a.window ? f0 - a.window + 1 : 0u) / BN);
+            it.wave_lo = (int)((q0 >= a.window ? q0 - a.window + 1 : 0u) / BN);
+            it.lo_end = q0 + MQ - 1 >= a.window ? (int)((q0 + MQ - 1 - a.window) / BN) : -1;
+        } else {
+            it.m_lo = 0;
+            it.wave_lo = 0;
+            it.lo_end = -1;
+        }
         return it;
     };
+    // window bounds; compile-time zero without a window
+    auto lo_of = [&](const Item& it) -> int { if constexpr (WIN) return it.m_lo; else return 0; };
+    auto wlo_of = [&](const Item& it) -> int { if constexpr (WIN) return it.wave_lo; else return 0; };
     // item taken in round r (snake order over the grid)
     auto item_at = [&](uint32_t r) -> uint32_t {
         const uint32_t g = gridDim.x;
@@ -332,15 +357,31 @@ sfa_prefill_kernel(const PrefillArgs a) {
     // rescaled either.  Only when a row's sum exceeds 2^8 (rare once the max
     // has settled) are the max test and the exponentials done again, which
     // gives exactly the result of always testing the max.
-    auto softmax = [&](f32x16 (&sacc)[BN / 32], int kt, bool diag, uint32_t qi, bf16x8 (&pf)[BN / 16]) {
+    auto softmax = [&](f32x16 (&sacc)[BN / 32], int kt, bool diag, bool lowmask, bool first,
+                       uint32_t qi, bf16x8 (&pf)[BN / 16]) {
+        // item (kb, it) holds key kt*BN + off + 4*hh with off = kb*32 + 8*(it/4)
+        // + it%4 (0..63, an inline constant): each mask is one compare of off
+        // against a per-lane threshold
+        const int rel = (int)qi - kt * BN - 4 * hh;
         if (diag) {
-            const uint32_t k0 = (uint32_t)kt * BN;
+            // keys later than the query
 #pragma unroll
             for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
                 for (int it = 0; it < 16; ++it) {
-                    const uint32_t key = k0 + kb * 32 + 8 * (it >> 2) + 4 * hh + (it & 3);
-                    if (key > qi) sacc[kb][it] = -INFINITY;
+                    const int off = kb * 32 + 8 * (it >> 2) + (it & 3);
+                    if (off > rel) sacc[kb][it] = -INFINITY;
+                }
+        }
+        if (WIN && lowmask) {
+            // keys at or below qi - W are outside the row's window
+            const int lim = rel - (int)a.window;
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+                for (int it = 0; it < 16; ++it) {
+                    const int off = kb * 32 + 8 * (it >> 2) + (it & 3);
+                    if (off <= lim) sacc[kb][it] = -INFINITY;
                 }
         }
         auto max_test = [&]() __attribute__((always_inline)) {
@@ -354,7 +395,8 @@ sfa_prefill_kernel(const PrefillArgs a) {
             else mx = halves_max(mx);
             if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.f) != 0) {
                 const float m_new = fmaxf(m_run, mx);
-                const float alpha = fast_exp2(m_run - m_new);
+                // a windowed row may have seen no visible key yet (m_new = -inf)
+                const float alpha = (WIN && m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
                 m_run = m_new;
                 l_run *= alpha;
 #pragma unroll
@@ -368,6 +410,7 @@ sfa_prefill_kernel(const PrefillArgs a) {
             // exponent argument has a two-operand form (v_fmamk_f32 / v_add_f32)
             float nm;
             asm("v_xor_b32 %0, 0x80000000, %1" : "=v"(nm) : "v"(m_run));
+            if constexpr (WIN) nm = m_run == -INFINITY ? 0.f : nm;   // such a row has only masked scores
             float rsp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c = 0; c < BN / 16; ++c) {
@@ -387,12 +430,16 @@ sfa_prefill_kernel(const PrefillArgs a) {
             return halves_sum((rsp[0] + rsp[1]) + (rsp[2] + rsp[3]));
         };
         float ts;
-        if (diag || kt == 0) {
+        if (diag || first) {
             max_test();
             ts = exps();
         } else {
             ts = exps();
-            if (__builtin_amdgcn_ballot_w64(ts > 256.f) != 0) {
+            // with a window, a row that has seen no visible key yet still has
+            // m_run = -inf, which cannot serve as the reference: retry too
+            bool retry = ts > 256.f;
+            if constexpr (WIN) retry = retry || m_run == -INFINITY;
+            if (__builtin_amdgcn_ballot_w64(retry) != 0) {
                 max_test();
                 ts = exps();
             }
@@ -426,12 +473,15 @@ sfa_prefill_kernel(const PrefillArgs a) {
 #pragma unroll
         for (int db = 0; db < DBLK; ++db) VA[rd * DBLK + db] = lds0 + voff[rd][db];
 
-    auto barrier_step = [&](int m, const Item& cur, uint32_t nid, bool more) {
+    // steps are counted from the item's first tile: r = m - m_lo picks the
+    // ring slots, m addresses the view
+    auto barrier_step = [&](int r, const Item& cur, uint32_t nid, bool more) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (m + 2 < cur.n_kt) issue(cur.kview, m + 2, kbuf(m + 2));
-        if (m + 1 < cur.n_kt) issue(cur.vview, m + 1, vbuf(m + 1));
+        const int m = lo_of(cur) + r;
+        if (m + 2 < cur.n_kt) issue(cur.kview, m + 2, kbuf(r + 2));
+        if (m + 1 < cur.n_kt) issue(cur.vview, m + 1, vbuf(r + 1));
         if (m == cur.n_kt - 1 && more) {
             // an opaque copy of the index keeps the address arithmetic here
             // (it is loop-invariant) from being hoisted and held in registers
@@ -440,24 +490,31 @@ sfa_prefill_kernel(const PrefillArgs a) {
             asm volatile("s_mov_b32 %0, %1" : "=s"(id2) : "s"(nid));
             const Item nx = make_item(id2);
             issue_q(id2);
-            issue(nx.kview, 0, kbuf(0));
-            if (nx.n_kt > 1) issue(nx.kview, 1, kbuf(1));
-            if (m & 1) issue(nx.vview, 0, vbuf(0));
+            issue(nx.kview, lo_of(nx), kbuf(0));
+            if (lo_of(nx) + 1 < nx.n_kt) issue(nx.kview, lo_of(nx) + 1, kbuf(1));
+            if (r & 1) issue(nx.vview, lo_of(nx), vbuf(0));
         }
     };
-    auto phase_a = [&](int m, const Item& cur) {
+    auto phase_a = [&](int r, const Item& cur) {
+        const int m = lo_of(cur) + r;
         const int last = cur.wave_kt - 1;      // the wave's diagonal tile takes the mask
-        if (m <= last) softmax(sc, m, m == last, cur.qi, pf);
+        if (m >= wlo_of(cur) && m <= last)
+            softmax(sc, m, m == last, WIN && m <= cur.lo_end, m == wlo_of(cur), cur.qi, pf);
     };
     // B(m) with m of parity PAR (fixes the LDS slots of K(m+1) and V(m))
-    auto phase_b = [&](auto par, int m, const Item& cur) {
+    auto phase_b = [&](auto par, int r, const Item& cur) {
         constexpr int PAR = decltype(par)::value;
+        const int m = lo_of(cur) + r;
         const int last = cur.wave_kt - 1;
         f32x16(&S)[BN / 32] = sc;
         f32x16(&O)[DBLK] = oacc;
         const bf16x8(&Q)[DSTEPS] = qf;
         const bf16x8(&P)[BN / 16] = pf;
-        if (m < last) {
+        // a wave computes P(m) for wave_lo <= m <= last and S(m+1) when m+1 is
+        // in that range too (without a window wave_lo = 0)
+        const bool do_pv = m >= wlo_of(cur) && m <= last;
+        const bool do_qk = m + 1 >= wlo_of(cur) && m < last;
+        if (do_pv && do_qk) {
             if constexpr (D == 128) {
                 if constexpr (PAR == 0) asm volatile(HD_ASM_FULL_D128_P0 : HD_ASM_OUTS_FULL_D128 : HD_ASM_INS_FULL_D128 : HD_ASM_CLOBBERS);
                 else asm volatile(HD_ASM_FULL_D128_P1 : HD_ASM_OUTS_FULL_D128 : HD_ASM_INS_FULL_D128 : HD_ASM_CLOBBERS);
@@ -465,7 +522,7 @@ sfa_prefill_kernel(const PrefillArgs a) {
                 if constexpr (PAR == 0) asm volatile(HD_ASM_FULL_D64_P0 : HD_ASM_OUTS_FULL_D64 : HD_ASM_INS_FULL_D64 : HD_ASM_CLOBBERS);
                 else asm volatile(HD_ASM_FULL_D64_P1 : HD_ASM_OUTS_FULL_D64 : HD_ASM_INS_FULL_D64 : HD_ASM_CLOBBERS);
             }
-        } else if (m == last) {
+        } else if (do_pv) {
             if constexpr (D == 128) {
                 if constexpr (PAR == 0) asm volatile(HD_ASM_PV_D128_P0 : HD_ASM_OUTS_PV_D128 : HD_ASM_INS_PV_D128 : HD_ASM_CLOBBERS);
                 else asm volatile(HD_ASM_PV_D128_P1 : HD_ASM_OUTS_PV_D128 : HD_ASM_INS_PV_D128 : HD_ASM_CLOBBERS);
@@ -473,13 +530,22 @@ sfa_prefill_kernel(const PrefillArgs a) {
                 if constexpr (PAR == 0) asm volatile(HD_ASM_PV_D64_P0 : HD_ASM_OUTS_PV_D64 : HD_ASM_INS_PV_D64 : HD_ASM_CLOBBERS);
                 else asm volatile(HD_ASM_PV_D64_P1 : HD_ASM_OUTS_PV_D64 : HD_ASM_INS_PV_D64 : HD_ASM_CLOBBERS);
             }
+        } else if (WIN && do_qk) {
+            // the tile before this wave's first one: only the scores of the next
+            if constexpr (D == 128) {
+                if constexpr (PAR == 0) asm volatile(HD_ASM_QK_D128_P0 : HD_ASM_OUTS_QK_D128 : HD_ASM_INS_QK_D128 : HD_ASM_CLOBBERS);
+                else asm volatile(HD_ASM_QK_D128_P1 : HD_ASM_OUTS_QK_D128 : HD_ASM_INS_QK_D128 : HD_ASM_CLOBBERS);
+            } else {
+                if constexpr (PAR == 0) asm volatile(HD_ASM_QK_D64_P0 : HD_ASM_OUTS_QK_D64 : HD_ASM_INS_QK_D64 : HD_ASM_CLOBBERS);
+                else asm volatile(HD_ASM_QK_D64_P1 : HD_ASM_OUTS_QK_D64 : HD_ASM_INS_QK_D64 : HD_ASM_CLOBBERS);
+            }
         }
     };
-    auto step = [&](auto par, int m, const Item& cur, uint32_t nid, bool more) {
-        if (wgrp) barrier_step(m, cur, nid, more);
-        phase_a(m, cur);
-        if (!wgrp) barrier_step(m, cur, nid, more);
-        phase_b(par, m, cur);
+    auto step = [&](auto par, int r, const Item& cur, uint32_t nid, bool more) {
+        if (wgrp) barrier_step(r, cur, nid, more);
+        phase_a(r, cur);
+        if (!wgrp) barrier_step(r, cur, nid, more);
+        phase_b(par, r, cur);
     };
 
     // ---- persistent loop over this workgroup's work items ----
@@ -488,9 +554,9 @@ sfa_prefill_kernel(const PrefillArgs a) {
     if (first >= a.n_items) return;            // uniform over the workgroup
     Item cur = make_item(first);
     issue_q(first);
-    issue(cur.kview, 0, kbuf(0));
-    issue(cur.vview, 0, vbuf(0));
-    if (cur.n_kt > 1) issue(cur.kview, 1, kbuf(1));
+    issue(cur.kview, lo_of(cur), kbuf(0));
+    issue(cur.vview, lo_of(cur), vbuf(0));
+    if (lo_of(cur) + 1 < cur.n_kt) issue(cur.kview, lo_of(cur) + 1, kbuf(1));
     for (;;) {
         const uint32_t nid = item_at(round + 1);
         const bool more = nid < a.n_items;
@@ -505,20 +571,25 @@ sfa_prefill_kernel(const PrefillArgs a) {
         m_run = -INFINITY;
         l_run = 0.f;
         if (cur.wave_kt > 0) {
+            // S of the item's first tile (K slot 0: the score product of parity 1)
             f32x16(&S)[BN / 32] = sc;
             const bf16x8(&Q)[DSTEPS] = qf;
-            if constexpr (D == 128) asm volatile(HD_ASM_QK_D128_P0 : HD_ASM_OUTS_QK_D128 : HD_ASM_INS_QK_D128 : HD_ASM_CLOBBERS);
-            else asm volatile(HD_ASM_QK_D64_P0 : HD_ASM_OUTS_QK_D64 : HD_ASM_INS_QK_D64 : HD_ASM_CLOBBERS);
+            if constexpr (D == 128) asm volatile(HD_ASM_QK_D128_P1 : HD_ASM_OUTS_QK_D128 : HD_ASM_INS_QK_D128 : HD_ASM_CLOBBERS);
+            else asm volatile(HD_ASM_QK_D64_P1 : HD_ASM_OUTS_QK_D64 : HD_ASM_INS_QK_D64 : HD_ASM_CLOBBERS);
         }
-        for (int m = 0; m < cur.n_kt; m += 2) {
-            step(std::integral_constant<int, 0>{}, m, cur, nid, more);
-            if (m + 1 < cur.n_kt) step(std::integral_constant<int, 1>{}, m + 1, cur, nid, more);
+        const int steps = cur.n_kt - lo_of(cur);
+        for (int r = 0; r < steps; r += 2) {
+            step(std::integral_constant<int, 0>{}, r, cur, nid, more);
+            if (r + 1 < steps) step(std::integral_constant<int, 1>{}, r + 1, cur, nid, more);
         }
         // every wave has finished reading this item's tiles: the ring is free
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        // V(0) of the next item, unless the final interval (odd F) already sent it
-        if (more && (cur.n_kt & 1)) issue(make_item(nid).vview, 0, vbuf(0));
+        // the next item's first V tile, unless the final interval (odd F) already sent it
+        if (more && (steps & 1)) {
+            const Item nx = make_item(nid);
+            issue(nx.vview, lo_of(nx), vbuf(0));
+        }
         store_out(cur.id, cur.qi);
         if (!more) break;
         cur = make_item(nid);
@@ -543,8 +614,9 @@ int device_cus() {
 hd_status launch_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          uint16_t* out, int64_t B, int32_t n, int64_t L, int32_t Hq,
                          int32_t Hkv, int32_t D, float scale, hipStream_t stream,
-                         bool within) {
-    if (B < 0 || L < 0 || n < 1 || Hq < 1 || Hkv < 1) return HD_ERR_SHAPE;
+                         bool within, int64_t window) {
+    // window: 0 = none (plain causal), else >= 1 rows of the view
+    if (B < 0 || L < 0 || n < 1 || Hq < 1 || Hkv < 1 || window < 0) return HD_ERR_SHAPE;
     if (Hq % Hkv != 0) return HD_ERR_SHAPE;
     if (D != 64 && D != 128) return HD_ERR_UNSUPPORTED;
     if (B == 0 || L == 0) return HD_OK;
@@ -580,12 +652,23 @@ hd_status launch_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v
     if (items > 0x7fffffffULL) return HD_ERR_UNSUPPORTED;
     a.n_items = (uint32_t)items;
     const uint64_t blocks = items < (uint64_t)device_cus() ? items : (uint64_t)device_cus();
+    // a window at least as long as the view masks nothing: the causal kernel
+    const bool win = window > 0 && window < (int64_t)a.len;
+    a.window = win ? (uint32_t)window : 0u;
     const int mode = a.c == 1.f ? kScaleLog2 : (scale == 1.f ? kScaleUnit : kScaleAny);
-    auto kern = D == 128
-        ? (mode == kScaleLog2 ? sfa_prefill_kernel<128, kScaleLog2>
-           : mode == kScaleUnit ? sfa_prefill_kernel<128, kScaleUnit> : sfa_prefill_kernel<128, kScaleAny>)
-        : (mode == kScaleLog2 ? sfa_prefill_kernel<64, kScaleLog2>
-           : mode == kScaleUnit ? sfa_prefill_kernel<64, kScaleUnit> : sfa_prefill_kernel<64, kScaleAny>);
+    auto pick = [&](auto d, auto w) {
+        constexpr int DD = decltype(d)::value;
+        constexpr bool WW = decltype(w)::value;
+        return mode == kScaleLog2 ? sfa_prefill_kernel<DD, kScaleLog2, WW>
+             : mode == kScaleUnit ? sfa_prefill_kernel<DD, kScaleUnit, WW>
+                                  : sfa_prefill_kernel<DD, kScaleAny, WW>;
+    };
+    using D128 = std::integral_constant<int, 128>;
+    using D64 = std::integral_constant<int, 64>;
+    using W1 = std::true_type;
+    using W0 = std::false_type;
+    auto kern = D == 128 ? (win ? pick(D128{}, W1{}) : pick(D128{}, W0{}))
+                         : (win ? pick(D64{}, W1{}) : pick(D64{}, W0{}));
     kern<<<dim3((uint32_t)blocks), dim3(THREADS), 0, stream>>>(a);
     return launch_status();
 }
@@ -600,7 +683,7 @@ extern "C" hd_status sfa_stream_attn(const uint16_t* q, const uint16_t* k,
                                      int32_t D, float softmax_scale,
                                      hipStream_t stream) {
     return hdsfa::launch_prefill(q, k, v, out, B, n, L, Hq, Hkv, D, softmax_scale,
-                                 stream, /*within=*/true);
+                                 stream, /*within=*/true, /*window=*/0);
 }
 
 extern "C" hd_status sfa_mix_attn(const uint16_t* q, const uint16_t* k,
@@ -608,6 +691,16 @@ extern "C" hd_status sfa_mix_attn(const uint16_t* q, const uint16_t* k,
                                   int32_t n, int64_t L, int32_t Hq, int32_t Hkv,
                                   int32_t D, float softmax_scale, hipStream_t stream) {
     return hdsfa::launch_prefill(q, k, v, out, B, n, L, Hq, Hkv, D, softmax_scale,
-                                 stream, /*within=*/false);
+                                 stream, /*within=*/false, /*window=*/0);
+}
+
+extern "C" hd_status sfa_mix_attn_window(const uint16_t* q, const uint16_t* k,
+                                         const uint16_t* v, uint16_t* out, int64_t B,
+                                         int32_t n, int64_t L, int32_t Hq, int32_t Hkv,
+                                         int32_t D, float softmax_scale, int64_t window,
+                                         hipStream_t stream) {
+    if (window < 1) return HD_ERR_SHAPE;
+    return hdsfa::launch_prefill(q, k, v, out, B, n, L, Hq, Hkv, D, softmax_scale,
+                                 stream, /*within=*/false, window);
 }
 

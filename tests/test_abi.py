@@ -30,7 +30,8 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
     assert set(names) == {"hd_status_string", "hd_abi_version", "hd_expand", "sfa_stream_attn",
-                          "sfa_mix_attn", "sfa_decode_workspace_size", "sfa_decode_step"}
+                          "sfa_mix_attn", "sfa_mix_attn_window", "sfa_decode_workspace_size",
+                          "sfa_decode_step"}
     for name in names:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, name
@@ -71,6 +72,16 @@ def test_prefill_validation(lib, fn):
     assert f(FAKE, FAKE + 8, FAKE, FAKE, 1, 2, 8, 4, 2, 128, 1.0, None) == SHAPE  # align
     assert f(None, None, None, None, 0, 2, 8, 4, 2, 128, 1.0, None) == OK
     assert f(None, None, None, None, 2, 2, 0, 4, 2, 128, 1.0, None) == OK
+
+
+def test_window_validation(lib):
+    f = lib.sfa_mix_attn_window
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 2, 8, 4, 2, 128, 1.0, 0, None) == SHAPE      # window < 1
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 2, 8, 4, 2, 128, 1.0, -5, None) == SHAPE
+    assert f(None, FAKE, FAKE, FAKE, 1, 2, 8, 4, 2, 128, 1.0, 16, None) == NULL
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 2, 8, 4, 3, 128, 1.0, 16, None) == SHAPE     # Hq % Hkv
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 2, 8, 4, 2, 96, 1.0, 16, None) == UNSUP      # D
+    assert f(None, None, None, None, 0, 2, 8, 4, 2, 128, 1.0, 16, None) == OK        # empty
 
 
 def test_decode_workspace_size(lib):

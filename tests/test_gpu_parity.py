@@ -130,6 +130,92 @@ def test_prefill_sweep(n, B, L, Hq, Hkv, D, mode):
     assert_close(f64(out), ref, f"sweep n={n} L={L} H={Hq}/{Hkv} D={D} mode={mode}")
 
 
+# sliding-window mixing: n, B, L, Hq, Hkv, D, W (W in interleaved positions)
+WINDOW_SWEEP = [
+    (4, 1, 40, 4, 1, 128, 1),          # own position only
+    (2, 1, 100, 8, 2, 128, 7),         # window inside one tile
+    (3, 1, 70, 16, 4, 128, 64),        # one tile wide
+    (4, 2, 65, 32, 8, 128, 65),        # a tile and one
+    (5, 1, 57, 8, 1, 64, 100),         # P=8 packing, D=64
+    (2, 1, 300, 4, 2, 64, 129),        # P=2 packing
+    (1, 1, 333, 2, 2, 128, 200),       # P=1 packing, n=1
+    (8, 1, 40, 16, 1, 128, 319),       # W = N - 1
+    (4, 1, 129, 32, 8, 128, 1024),     # W > N: the causal kernel
+]
+
+
+@pytest.mark.parametrize("n,B,L,Hq,Hkv,D,W", WINDOW_SWEEP)
+def test_prefill_window_sweep(n, B, L, Hq, Hkv, D, W):
+    seed = 4000 + 31 * n + 7 * L + W
+    N = n * L
+    q = _rand((B, N, Hq, D), D ** -0.5, seed, "cpu")
+    k = _rand((B, N, Hkv, D), 1.0, seed + 1, "cpu")
+    v = _rand((B, N, Hkv, D), 1.0, seed + 2, "cpu")
+    out = hd.mix_attn_window(q.to(DEV), k.to(DEV), v.to(DEV), n, 1.0, W)
+    ref = oracle.prefill_ref(si.bits(q), si.bits(k), si.bits(v), n, MIX, 1.0, window=W)
+    assert_close(f64(out), ref, f"window W={W} n={n} L={L} H={Hq}/{Hkv} D={D}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_window_scale_modes(D):
+    """The same windowed product through the three scale modes of the kernel."""
+    n, B, L, Hq, Hkv, W = 3, 1, 90, 8, 2, 77
+    seed = 4500 + D
+    N = n * L
+    q = _rand((B, N, Hq, D), 1.0, seed, "cpu")
+    k = _rand((B, N, Hkv, D), 1.0, seed + 1, "cpu")
+    v = _rand((B, N, Hkv, D), 1.0, seed + 2, "cpu")
+    scale = D ** -0.5
+    ref = oracle.prefill_ref(si.bits(q), si.bits(k), si.bits(v), n, MIX, scale, window=W)
+    kd, vd = k.to(DEV), v.to(DEV)
+    out0 = hd.mix_attn_window(q.to(DEV), kd, vd, n, scale, W)
+    assert_close(f64(out0), ref, f"window any-scale D={D}")
+    out1 = hd.mix_attn_window((q.float() * scale).to(torch.bfloat16).to(DEV), kd, vd, n, 1.0, W)
+    assert_close(f64(out1), ref, f"window unit-scale D={D}")
+    out2 = hd.mix_attn_window((q.float() * (scale * si.LOG2E)).to(torch.bfloat16).to(DEV), kd, vd,
+                              n, si.LN2, W)
+    assert_close(f64(out2), ref, f"window log2 units D={D}")
+
+
+def test_prefill_window_one_returns_v_exactly():
+    """W = 1: one visible key with probability exactly 1, so the output is that
+    key's value row, bit for bit."""
+    n, B, L, Hq, Hkv, D = 4, 1, 70, 8, 2, 128
+    N = n * L
+    q = _rand((B, N, Hq, D), 1.0, 4600)
+    k = _rand((B, N, Hkv, D), 1.0, 4601)
+    v = _rand((B, N, Hkv, D), 1.0, 4602)
+    out = hd.mix_attn_window(q, k, v, n, 1.0, 1)
+    want = v.repeat_interleave(Hq // Hkv, dim=2)
+    assert torch.equal(out.view(torch.int16), want.view(torch.int16))
+
+
+def test_prefill_window_at_least_n_is_mix_bitwise():
+    cfg = si.TINY
+    q, k, v = (t.to(DEV) for t in si.prefill_qkv(cfg))
+    a = hd.mix_attn(q, k, v, cfg.n, cfg.scale)
+    for W in (cfg.N, cfg.N + 1, 1 << 40):
+        b = hd.mix_attn_window(q, k, v, cfg.n, cfg.scale, W)
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), W
+
+
+def test_prefill_window_full_size_sampled():
+    """The n4 workload's mixing layer with a window of 1024 positions (256
+    tokens x 4 streams), sampled rows and heads, in the bench's launch."""
+    cfg, W = si.N4, 1024
+    q, k, v = si.prefill_qkv(cfg, device=DEV)
+    out = hd.mix_attn_window(q, k, v, cfg.n, cfg.scale, W)
+    torch.cuda.synchronize()
+    rows = _sample_rows(cfg.N, cfg.n, 40, 17)
+    rows = np.unique(np.concatenate([rows, [W - 2, W - 1, W, W + 1, W + 63, W + 64]]))
+    G = cfg.Hq // cfg.Hkv
+    heads = sorted({0, G - 1, G, cfg.Hq - 1})
+    ref = oracle.prefill_ref(si.bits(q[:1].cpu()), si.bits(k[:1].cpu()), si.bits(v[:1].cpu()),
+                             cfg.n, MIX, cfg.scale, rows=rows, heads=heads, window=W)
+    got = f64(out[:1, torch.as_tensor(rows, device=DEV)][:, :, heads].cpu())
+    assert_close(got, ref, f"n4 window {W} sampled")
+
+
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("mode", [WITHIN, MIX])
 def test_prefill_nonunit_scale(D, mode):
