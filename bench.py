@@ -137,14 +137,38 @@ def bench_prefill(args, torch, hd, si):
     ew[1].record()
     torch.cuda.synchronize()
     t_mw = ew[0].elapsed_time(ew[1]) / args.steps
+    # final-stream rows of the expanded hidden states (the LM head's input)
+    fsr = torch.empty((cfg.B, cfg.L, cfg.hidden), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        hd.final_stream_rows(x, cfg.n, out=fsr)
+    ew[0].record()
+    for _ in range(args.steps):
+        hd.final_stream_rows(x, cfg.n, out=fsr)
+    ew[1].record()
+    torch.cuda.synchronize()
+    t_fs = ew[0].elapsed_time(ew[1]) / args.steps
+    fs_bytes = 2 * cfg.B * cfg.L * cfg.hidden * 2
+    # Cyclic Replication Initialization 2 -> 4 tables in place (after the step
+    # timings: tables 2 and 3 become copies of 0 and 1)
+    for _ in range(2):
+        hd.cyclic_replicate(tab[:2], cfg.n, out=tab)
+    ew[0].record()
+    reps = max(1, args.steps // 4)
+    for _ in range(reps):
+        hd.cyclic_replicate(tab[:2], cfg.n, out=tab)
+    ew[1].record()
+    torch.cuda.synchronize()
+    t_cr = ew[0].elapsed_time(ew[1]) / reps
+    cr_bytes = 2 * (cfg.n - 2) * cfg.vocab * cfg.hidden * 2
 
     fw = attn_flops(cfg.B, cfg.n, cfg.L, cfg.Hq, cfg.D, "within")
     fm = attn_flops(cfg.B, cfg.n, cfg.L, cfg.Hq, cfg.D, "mix")
     fmw = attn_flops(cfg.B, cfg.n, cfg.L, cfg.Hq, cfg.D, "mix", WINDOW)
     exp_bytes = cfg.B * cfg.N * cfg.hidden * 2 * 2 + cfg.B * cfg.L * 4
     res = dict(cfg=cfg, ms_step=ms_step, t_exp=t_exp, t_w=t_w, t_m=t_m, fw=fw, fm=fm,
-               exp_bytes=exp_bytes, t_mw=t_mw, fmw=fmw)
-    del ids, tab, q, k, v, x, ow, om
+               exp_bytes=exp_bytes, t_mw=t_mw, fmw=fmw, t_fs=t_fs, fs_bytes=fs_bytes,
+               t_cr=t_cr, cr_bytes=cr_bytes)
+    del ids, tab, q, k, v, x, ow, om, fsr
     torch.cuda.empty_cache()
     return res
 
@@ -345,6 +369,15 @@ def main():
                                 "window": WINDOW, "useful_gflop": round(pf["fmw"] / 1e9, 3),
                                 "note": "sliding-window mixing layer, same n4 inputs; "
                                         "not part of the step"},
+        "hd_final_stream_rows": {"ms": round(pf["t_fs"], 4), "bound": "hbm",
+                                 "achieved": round(pf["fs_bytes"] / (pf["t_fs"] * 1e-3) / 1e9, 1),
+                                 "unit": "GB/s", "peak": PEAK_HBM_GBS,
+                                 "note": "[2, 4096, 4096] -> [2, 1024, 4096]; not part of the step"},
+        "hd_cyclic_replicate": {"ms": round(pf["t_cr"], 4), "bound": "hbm",
+                                "achieved": round(pf["cr_bytes"] / (pf["t_cr"] * 1e-3) / 1e9, 1),
+                                "unit": "GB/s", "peak": PEAK_HBM_GBS,
+                                "note": "2 -> 4 tables of 151936 x 4096 in place (2.49 GB read + "
+                                        "written); not part of the step"},
     }
     for kk in kernels.values():
         kk["frac"] = round(kk["achieved"] / kk["peak"], 4)

@@ -81,6 +81,40 @@ hd_status hd_expand(const int32_t* ids, int64_t B, int64_t L,
                     uint16_t* out, int32_t* err_flag, hipStream_t stream);
 
 /*
+ * hd_final_stream_rows -- the rows the next-token loss reads.  Review, section
+ * Method: cross-entropy is applied only at the final stream's positions, the
+ * first n-1 streams being latent computation states.
+ *
+ *   out[b, t, :] = x[b, t*n + n-1, :]   for b < B, t < L
+ *
+ *   x      bf16 [B, n*L, H]   hidden states of the expanded sequence
+ *   out    bf16 [B, L, H]     must not overlap x
+ * Pure copy (bit-identical).  H must be a multiple of 8, x and out 16-byte
+ * aligned (HD_ERR_SHAPE otherwise); B*L*H/8 must stay below 2^32
+ * (HD_ERR_UNSUPPORTED).
+ */
+hd_status hd_final_stream_rows(const uint16_t* x, int64_t B, int32_t n, int64_t L,
+                               int64_t H, uint16_t* out, hipStream_t stream);
+
+/*
+ * hd_cyclic_replicate -- Cyclic Replication Initialization.  Review, section
+ * Method: the expansion factor grows 1 -> 2 -> 4 -> 8, and when it grows the
+ * new embedding tables are copies of the existing ones.
+ *
+ *   out[s] = tables[s mod n_old]   for s < n_new
+ *
+ *   tables bf16 [n_old, V, H]
+ *   out    bf16 [n_new, V, H]; either out == tables (growth in place: the
+ *          allocation holds n_new tables, the first n_old are left as they
+ *          are and only tables n_old .. n_new-1 are written) or a buffer that
+ *          does not overlap tables (HD_ERR_SHAPE on partial overlap)
+ * Pure copy (bit-identical).  H must be a multiple of 8, pointers 16-byte
+ * aligned; V*H/8 below 2^32 and n_new <= 65535 (HD_ERR_UNSUPPORTED).
+ */
+hd_status hd_cyclic_replicate(const uint16_t* tables, int32_t n_old, int64_t V, int64_t H,
+                              uint16_t* out, int32_t n_new, hipStream_t stream);
+
+/*
  * sfa_stream_attn -- within-stream causal attention over the expanded
  * sequence (prefill).  Review, section Method: most layers attend only within
  * their own stream, at a cost of order n*L^2.

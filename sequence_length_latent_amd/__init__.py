@@ -15,8 +15,9 @@ import torch
 
 from ._lib import HDError, check, load  # noqa: F401
 
-__all__ = ["expand", "stream_attn", "mix_attn", "mix_attn_window", "decode_workspace_size",
-           "decode_step", "HDError", "load", "WITHIN", "MIX"]
+__all__ = ["expand", "final_stream_rows", "cyclic_replicate", "stream_attn", "mix_attn",
+           "mix_attn_window", "decode_workspace_size", "decode_step", "HDError", "load",
+           "WITHIN", "MIX"]
 
 WITHIN = 0
 MIX = 1
@@ -60,6 +61,39 @@ def expand(ids: torch.Tensor, tables: torch.Tensor, out: torch.Tensor | None = N
     st = load().hd_expand(ids.data_ptr(), B, L, tables.data_ptr(), n, V, H, out.data_ptr(),
                           flag or None, _stream())
     check("hd_expand", st)
+    return out
+
+
+def final_stream_rows(x, n: int, out=None):
+    """Rows of the final stream: out[b, t] = x[b, t*n + n-1].  x [B, n*L, H] bf16."""
+    _need(x, "x", torch.bfloat16, 3)
+    B, N, H = x.shape
+    if n < 1 or N % n:
+        raise ValueError(f"sequence length {N} is not a multiple of n={n}")
+    if out is None:
+        out = torch.empty((B, N // n, H), dtype=x.dtype, device=x.device)
+    _need(out, "out", torch.bfloat16, 3)
+    if tuple(out.shape) != (B, N // n, H):
+        raise ValueError("out must be [B, L, H]")
+    st = load().hd_final_stream_rows(x.data_ptr(), B, n, N // n, H, out.data_ptr(), _stream())
+    check("hd_final_stream_rows", st)
+    return out
+
+
+def cyclic_replicate(tables, n_new: int, out=None):
+    """Cyclic Replication Initialization: out[s] = tables[s % n_old], s < n_new.
+    tables [n_old, V, H] bf16.  With out=None a new [n_new, V, H] tensor is
+    returned; an ``out`` whose storage starts at ``tables`` grows in place."""
+    _need(tables, "tables", torch.bfloat16, 3)
+    n_old, V, H = tables.shape
+    if out is None:
+        out = torch.empty((n_new, V, H), dtype=tables.dtype, device=tables.device)
+    _need(out, "out", torch.bfloat16, 3)
+    if tuple(out.shape) != (n_new, V, H):
+        raise ValueError("out must be [n_new, V, H]")
+    st = load().hd_cyclic_replicate(tables.data_ptr(), n_old, V, H, out.data_ptr(), n_new,
+                                    _stream())
+    check("hd_cyclic_replicate", st)
     return out
 
 

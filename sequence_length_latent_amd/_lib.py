@@ -18,6 +18,8 @@ SIGNATURES = {
     "hd_status_string": (C.c_char_p, [C.c_int]),
     "hd_abi_version": (C.c_int, []),
     "hd_expand": (C.c_int, [_vp, _i64, _i64, _vp, _i32, _i64, _i64, _vp, _vp, _vp]),
+    "hd_final_stream_rows": (C.c_int, [_vp, _i64, _i32, _i64, _i64, _vp, _vp]),
+    "hd_cyclic_replicate": (C.c_int, [_vp, _i32, _i64, _i64, _vp, _i32, _vp]),
     "sfa_stream_attn": (C.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i64, _i32, _i32, _i32,
                                   _f32, _vp]),
     "sfa_mix_attn": (C.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i64, _i32, _i32, _i32,

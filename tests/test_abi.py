@@ -29,7 +29,8 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert set(names) == {"hd_status_string", "hd_abi_version", "hd_expand", "sfa_stream_attn",
+    assert set(names) == {"hd_status_string", "hd_abi_version", "hd_expand",
+                          "hd_final_stream_rows", "hd_cyclic_replicate", "sfa_stream_attn",
                           "sfa_mix_attn", "sfa_mix_attn_window", "sfa_decode_workspace_size",
                           "sfa_decode_step"}
     for name in names:
@@ -72,6 +73,22 @@ def test_prefill_validation(lib, fn):
     assert f(FAKE, FAKE + 8, FAKE, FAKE, 1, 2, 8, 4, 2, 128, 1.0, None) == SHAPE  # align
     assert f(None, None, None, None, 0, 2, 8, 4, 2, 128, 1.0, None) == OK
     assert f(None, None, None, None, 2, 2, 0, 4, 2, 128, 1.0, None) == OK
+
+
+def test_stream_copy_validation(lib):
+    f, c = lib.hd_final_stream_rows, lib.hd_cyclic_replicate
+    assert f(FAKE, 1, 0, 4, 8, FAKE + 4096, None) == SHAPE         # n
+    assert f(FAKE, 1, 2, 4, 12, FAKE + 4096, None) == SHAPE        # H % 8
+    assert f(FAKE + 8, 1, 2, 4, 8, FAKE + 4096, None) == SHAPE     # alignment
+    assert f(FAKE, 1, 2, 4, 8, FAKE + 16, None) == SHAPE           # out overlaps x
+    assert f(None, 1, 2, 4, 8, FAKE, None) == NULL
+    assert f(None, 0, 2, 4, 8, None, None) == OK                   # empty
+    assert c(FAKE, 0, 5, 8, FAKE + 4096, 2, None) == SHAPE         # n_old
+    assert c(FAKE, 2, 5, 8, FAKE + 16, 4, None) == SHAPE           # partial overlap
+    assert c(FAKE, 2, 5, 12, FAKE + 4096, 4, None) == SHAPE        # H % 8
+    assert c(None, 2, 5, 8, FAKE, 4, None) == NULL
+    assert c(FAKE, 4, 5, 8, FAKE, 2, None) == OK                   # in place, nothing to add
+    assert c(None, 2, 0, 8, None, 4, None) == OK                   # empty tables
 
 
 def test_window_validation(lib):

@@ -91,6 +91,63 @@ def test_expand_n4_full_size_sampled():
 
 
 # ---------------------------------------------------------------------------
+# final-stream rows and cyclic replication (bit-exact)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B,n,L,H", [(1, 1, 5, 8), (2, 4, 33, 136), (3, 8, 7, 64), (1, 3, 1000, 24)])
+def test_final_stream_rows_bit_exact(B, n, L, H):
+    x = _rand((B, n * L, H), 1.0, 5000 + n + L)
+    out = hd.final_stream_rows(x, n)
+    ref = oracle.final_stream_rows_ref(si.bits(x), n)
+    assert np.array_equal(si.bits(out), ref)
+
+
+def test_final_stream_rows_n4_full_size():
+    """The n4 workload's expanded hidden size: [2, 4096, 4096] -> [2, 1024, 4096]."""
+    cfg = si.N4
+    x = _rand((cfg.B, cfg.N, cfg.hidden), 1.0, 5100)
+    out = hd.final_stream_rows(x, cfg.n)
+    ref = oracle.final_stream_rows_ref(si.bits(x), cfg.n)
+    assert np.array_equal(si.bits(out), ref)
+
+
+@pytest.mark.parametrize("n_old,n_new,V,H", [(1, 2, 7, 8), (2, 4, 100, 64), (3, 8, 33, 24),
+                                             (4, 2, 10, 16), (2, 5, 1000, 4096)])
+def test_cyclic_replicate_bit_exact(n_old, n_new, V, H):
+    tab = _rand((n_old, V, H), 0.02, 5200 + n_old * 10 + n_new)
+    out = hd.cyclic_replicate(tab, n_new)
+    ref = oracle.cyclic_replicate_ref(si.bits(tab), n_new)
+    assert np.array_equal(si.bits(out), ref)
+
+
+def test_cyclic_replicate_in_place_growth():
+    """1 -> 2 -> 4 -> 8 in one allocation (the pages' schedule): table 0 is
+    never written and every table ends a copy of it."""
+    V, H = 257, 128
+    buf = torch.zeros((8, V, H), dtype=torch.bfloat16, device=DEV)
+    buf[0] = _rand((V, H), 0.02, 5300)
+    before = si.bits(buf[0:1]).copy()
+    for n_old, n_new in ((1, 2), (2, 4), (4, 8)):
+        hd.cyclic_replicate(buf[:n_old], n_new, out=buf[:n_new])
+        ref = oracle.cyclic_replicate_ref(before, n_new)
+        assert np.array_equal(si.bits(buf[:n_new]), ref), (n_old, n_new)
+
+
+def test_cyclic_replicate_n4_vocab_sampled():
+    """The n4 workload's tables: 2 -> 4 tables of 151936 x 4096 in place; all
+    rows compared on the GPU, sampled rows against the oracle."""
+    cfg = si.N4
+    buf = torch.empty((4, cfg.vocab, cfg.hidden), dtype=torch.bfloat16, device=DEV)
+    buf[:2] = si.tables(2, cfg.vocab, cfg.hidden, cfg.table_std, 5400, device=DEV)
+    hd.cyclic_replicate(buf[:2], 4, out=buf)
+    torch.cuda.synchronize()
+    assert torch.equal(buf[2].view(torch.int16), buf[0].view(torch.int16))
+    assert torch.equal(buf[3].view(torch.int16), buf[1].view(torch.int16))
+    rows = torch.tensor([0, 1, 77, 4095, cfg.vocab - 1], device=DEV)
+    ref = oracle.cyclic_replicate_ref(si.bits(buf[:2, rows]), 4)
+    assert np.array_equal(si.bits(buf[:, rows]), ref)
+
+
+# ---------------------------------------------------------------------------
 # prefill attention
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("mode", [WITHIN, MIX])

@@ -114,6 +114,17 @@ def test_final_stream_rows_and_cyclic_replication():
     rep = oracle.cyclic_replicate_ref(tab, 4)
     assert rep.shape == (4, 5, 3)
     assert np.array_equal(rep[2], tab[0]) and np.array_equal(rep[3], tab[1])
+    # n = 1: the final stream is every row
+    y = np.arange(2 * 5 * 4).reshape(2, 5, 4)
+    assert np.array_equal(oracle.final_stream_rows_ref(y, 1), y)
+    # growth that is not a doubling: 3 -> 8 tables cycle 0,1,2,0,1,2,0,1
+    tab3 = np.arange(3 * 2 * 2).reshape(3, 2, 2)
+    rep8 = oracle.cyclic_replicate_ref(tab3, 8)
+    assert [int(r[0, 0]) for r in rep8] == [0, 4, 8, 0, 4, 8, 0, 4]
+    # 1 -> 2 -> 4 -> 8 (the pages' schedule) leaves every table a copy of table 0
+    t1 = np.arange(6).reshape(1, 2, 3)
+    t8 = oracle.cyclic_replicate_ref(oracle.cyclic_replicate_ref(oracle.cyclic_replicate_ref(t1, 2), 4), 8)
+    assert all(np.array_equal(t, t1[0]) for t in t8)
 
 
 # ---------------------------------------------------------------------------
