@@ -6,6 +6,7 @@ the CPU-baseline leg of ``bench.py``; never by the library.
 from .sfa import (  # noqa: F401
     MIX,
     WITHIN,
+    attention_backward_head,
     attention_rows,
     bf16_bits_to_f64,
     count_pairs,
@@ -15,6 +16,7 @@ from .sfa import (  # noqa: F401
     expand_ref,
     expanded_position,
     final_stream_rows_ref,
+    prefill_backward_ref,
     prefill_ref,
     useful_flops,
     visible,

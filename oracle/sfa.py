@@ -232,6 +232,86 @@ def prefill_ref(q, k, v, n, mode, scale, rows=None, heads=None, batches=None,
 
 
 # ---------------------------------------------------------------------------
+# (3b) Gradients of a prefill layer (training)
+# ---------------------------------------------------------------------------
+def attention_backward_head(qf, kf, vf, dof, n, mode, scale, window=None, chunk=512):
+    """Gradients of O = softmax(scale * Q K^T + mask) V for one query head,
+    float64 in and out, written out from the definition (the review's
+    *Results* numbers are training costs of the expanded sequence, so the
+    layer's gradient is part of the method's cost).  For queries i, keys j:
+
+        P = masked softmax of scale * Q K^T (rows i),   O = P V
+        dV = P^T dO,   dP = dO V^T,   delta_i = sum_d dO_id O_id
+        dS = P * (dP - delta)        (the softmax Jacobian applied to dP)
+        dQ = scale * dS K,   dK = scale * dS^T Q
+
+    qf, dof : [N, D] queries and upstream gradient of the output
+    kf, vf  : [N, D] keys and values (positions 0..N-1)
+    returns (dq [N, D], dk [N, D], dv [N, D], lse [N]) with lse_i the natural
+    log of sum over visible j of exp(scale * q_i . k_j).
+    """
+    N = qf.shape[0]
+    dq = np.zeros_like(qf)
+    dk = np.zeros_like(kf)
+    dv = np.zeros_like(vf)
+    lse = np.zeros(N)
+    j = np.arange(N)[None, :]
+    for r0 in range(0, N, chunk):
+        r = np.arange(r0, min(N, r0 + chunk))
+        s = scale * (qf[r] @ kf.T)
+        s = np.where(visible(r[:, None], j, n, mode, window), s, -np.inf)
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(s - m)
+        z = e.sum(axis=1, keepdims=True)
+        p = e / z
+        lse[r] = (m + np.log(z))[:, 0]
+        o = p @ vf
+        delta = np.sum(dof[r] * o, axis=1, keepdims=True)
+        dp = dof[r] @ vf.T
+        ds = p * (dp - delta)
+        dq[r] = scale * (ds @ kf)
+        dk += scale * (ds.T @ qf[r])
+        dv += p.T @ dof[r]
+    return dq, dk, dv, lse
+
+
+def prefill_backward_ref(q, k, v, dout, n, mode, scale, window=None, heads=None, batches=None):
+    """Gradients of a prefill SFA layer (the forward is ``prefill_ref``).
+
+    q, dout : bf16 bits [B, N, Hq, D];  k, v : bf16 bits [B, N, Hkv, D]
+    heads   : optional KV heads to compute (default all); batches likewise
+    returns float64 (dq [b, N, Hq', D], dk [b, N, Hkv', D], dv [b, N, Hkv', D],
+    lse [b, N, Hq']) over the selected batches and KV heads (Hq' = G * Hkv'),
+    query heads in order.  dK and dV of KV head g sum the contributions of its
+    G query heads (reading R6).
+    """
+    q, k, v, dout = (np.asarray(t) for t in (q, k, v, dout))
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    heads = list(range(Hkv)) if heads is None else list(heads)
+    batches = list(range(B)) if batches is None else list(batches)
+    dq = np.zeros((len(batches), N, G * len(heads), D))
+    dk = np.zeros((len(batches), N, len(heads), D))
+    dv = np.zeros_like(dk)
+    lse = np.zeros((len(batches), N, G * len(heads)))
+    for bi, b in enumerate(batches):
+        for gi, g in enumerate(heads):
+            kf = bf16_bits_to_f64(k[b, :, g, :])
+            vf = bf16_bits_to_f64(v[b, :, g, :])
+            for hh in range(G):
+                h = g * G + hh
+                r = attention_backward_head(bf16_bits_to_f64(q[b, :, h, :]), kf, vf,
+                                            bf16_bits_to_f64(dout[b, :, h, :]), n, mode,
+                                            scale, window)
+                dq[bi, :, gi * G + hh] = r[0]
+                dk[bi, :, gi] += r[1]
+                dv[bi, :, gi] += r[2]
+                lse[bi, :, gi * G + hh] = r[3]
+    return dq, dk, dv, lse
+
+
+# ---------------------------------------------------------------------------
 # (4) Decode step over the retained KV cache
 # ---------------------------------------------------------------------------
 def decode_append_ref(k_cache, v_cache, k_new, v_new, tokens_before, n):

@@ -200,6 +200,99 @@ def test_prefill_matches_brute_force(n, L, Hq, Hkv, D, mode):
 
 
 # ---------------------------------------------------------------------------
+# gradients of a prefill layer
+# ---------------------------------------------------------------------------
+def _autograd_grads(qf, kf, vf, dof, n, mode, scale, window=None):
+    """float64 torch autograd through masked softmax attention of one head."""
+    N = qf.shape[0]
+    q = torch.tensor(qf, requires_grad=True)
+    k = torch.tensor(kf, requires_grad=True)
+    v = torch.tensor(vf, requires_grad=True)
+    mask = torch.tensor(sfa.visible(np.arange(N)[:, None], np.arange(N)[None, :], n, mode, window))
+    s = (scale * q @ k.T).masked_fill(~mask, float("-inf"))
+    o = torch.softmax(s, dim=1) @ v
+    o.backward(torch.tensor(dof))
+    lse = torch.logsumexp(s, dim=1)
+    return q.grad.numpy(), k.grad.numpy(), v.grad.numpy(), lse.detach().numpy()
+
+
+@pytest.mark.parametrize("n,L,mode,window", [(1, 9, MIX, None), (2, 6, WITHIN, None),
+                                             (3, 5, MIX, None), (4, 4, MIX, 5), (2, 7, WITHIN, None)])
+def test_backward_matches_autograd(n, L, mode, window):
+    rng = np.random.default_rng(900 + n * 10 + L)
+    N, D = n * L, 8
+    qf, kf, vf, dof = (rng.standard_normal((N, D)) for _ in range(4))
+    got = sfa.attention_backward_head(qf, kf, vf, dof, n, mode, 0.7, window, chunk=5)
+    want = _autograd_grads(qf, kf, vf, dof, n, mode, 0.7, window)
+    for g, w in zip(got, want):
+        np.testing.assert_allclose(g, w, rtol=0, atol=1e-12)
+
+
+def test_backward_matches_finite_differences():
+    """Central differences of L = sum(dO * O) through the forward definition
+    (attention_rows), entry by entry, against the backward formulas."""
+    rng = np.random.default_rng(950)
+    n, L, D, scale = 2, 5, 4, 0.9
+    N = n * L
+    qf, kf, vf, dof = (rng.standard_normal((N, D)) for _ in range(4))
+
+    def loss(mode, qq, kk, vv):
+        o, _ = sfa.attention_rows(qq, np.arange(N), kk, vv, n, mode, scale)
+        return float(np.sum(dof * o))
+
+    eps = 1e-6
+    for mode in (WITHIN, MIX):
+        dq, dk, dv, _ = sfa.attention_backward_head(qf, kf, vf, dof, n, mode, scale)
+        for which, grad in ((0, dq), (1, dk), (2, dv)):
+            for (i, d) in ((0, 0), (3, 1), (N - 1, 3), (N // 2, 2)):
+                args = [qf.copy(), kf.copy(), vf.copy()]
+                args[which][i, d] += eps
+                lp = loss(mode, *args)
+                args[which][i, d] -= 2 * eps
+                lm = loss(mode, *args)
+                assert abs((lp - lm) / (2 * eps) - grad[i, d]) < 1e-7, (mode, which, i, d)
+
+
+def test_backward_invariants():
+    """Shifting every key by the same vector leaves each row's softmax
+    unchanged (the shift adds a per-row constant to the scores), so the key
+    gradients of each query row sum to zero; and with dO = V-independent
+    constant rows the value gradient is the column sums of P times dO."""
+    rng = np.random.default_rng(960)
+    n, L, D = 3, 6, 8
+    N = n * L
+    qf, kf, vf, dof = (rng.standard_normal((N, D)) for _ in range(4))
+    for mode in (WITHIN, MIX):
+        dq, dk, dv, lse = sfa.attention_backward_head(qf, kf, vf, dof, n, mode, 0.5)
+        np.testing.assert_allclose(dk.sum(axis=0), 0.0, atol=1e-12)
+        _, p = sfa.attention_rows(qf, np.arange(N), kf, vf, n, mode, 0.5)
+        ones = np.ones((N, D))
+        _, _, dv1, _ = sfa.attention_backward_head(qf, kf, vf, ones, n, mode, 0.5)
+        np.testing.assert_allclose(dv1, np.repeat(p.sum(axis=0)[:, None], D, axis=1), atol=1e-12)
+        s = 0.5 * qf @ kf.T
+        mask = sfa.visible(np.arange(N)[:, None], np.arange(N)[None, :], n, mode)
+        np.testing.assert_allclose(np.exp(np.where(mask, s, -np.inf) - lse[:, None]).sum(axis=1),
+                                   1.0, atol=1e-12)
+
+
+def test_backward_ref_sums_query_heads_into_kv_heads():
+    rng = np.random.default_rng(970)
+    n, L, Hq, Hkv, D = 2, 4, 4, 2, 8
+    q, k, v = _qkv(rng, 1, n, L, Hq, Hkv, D)
+    do = _rand_bits(rng, (1, n * L, Hq, D))
+    dq, dk, dv, lse = oracle.prefill_backward_ref(q, k, v, do, n, MIX, 0.6)
+    for g in range(Hkv):
+        acc = np.zeros((n * L, D))
+        for hh in range(Hq // Hkv):
+            h = g * (Hq // Hkv) + hh
+            r = sfa.attention_backward_head(_f(q)[0, :, h], _f(k)[0, :, g], _f(v)[0, :, g],
+                                            _f(do)[0, :, h], n, MIX, 0.6)
+            np.testing.assert_allclose(dq[0, :, h], r[0], atol=0)
+            acc += r[1]
+        np.testing.assert_allclose(dk[0, :, g], acc, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
 # sliding-window mixing (reading R13)
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("N,W", [(1, 1), (17, 1), (17, 5), (64, 64), (64, 100), (130, 64),
