@@ -171,6 +171,65 @@ hd_status sfa_mix_attn_window(const uint16_t* q, const uint16_t* k, const uint16
                               int64_t window, hipStream_t stream);
 
 /*
+ * sfa_attn_fwd -- a prefill layer's forward with its log-sum-exp (training).
+ * Review, sections Method and Results: the model trains on the expanded
+ * sequence, and the backward pass needs each query row's softmax statistics.
+ * Same output as sfa_stream_attn (mode 0) or sfa_mix_attn (mode 1), plus
+ *
+ *   lse[b, h, i] = log( sum over visible j of exp(scale * q[b,i,h] . k[b,j,g]) )
+ *
+ *   lse   fp32 [B, Hq, n*L] (natural log), 4-byte aligned, or NULL (then the
+ *         call is exactly the plain forward)
+ *   mode  0 within-stream, 1 mixing (HD_ERR_SHAPE otherwise)
+ * Other arguments, layouts and errors as sfa_stream_attn.
+ */
+hd_status sfa_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                       uint16_t* out, float* lse, int64_t B, int32_t n, int64_t L,
+                       int32_t Hq, int32_t Hkv, int32_t D, float softmax_scale,
+                       int32_t mode, hipStream_t stream);
+
+/*
+ * sfa_attn_bwd_workspace_size -- bytes of device workspace sfa_attn_bwd needs
+ * (one fp32 per query row and head).  Returns 0 for invalid sizes.
+ */
+size_t sfa_attn_bwd_workspace_size(int64_t B, int32_t n, int64_t L, int32_t Hq);
+
+/*
+ * sfa_attn_bwd -- gradients of a prefill layer (within-stream or mixing)
+ * with respect to q, k and v.  With P the masked softmax of scale * Q K^T
+ * (the same visibility as the forward, rebuilt from lse) and dO the upstream
+ * gradient:
+ *
+ *   dP = dO V^T,   delta_i = sum_j P_ij dP_ij,   dS = P * (dP - delta)
+ *   dq = scale * dS K,   dk = scale * dS^T Q,   dv = P^T dO
+ *
+ * (delta equals dO_i . O_i for the exact O; it is summed from P and dP so
+ * that the bf16 rounding of the forward's output does not enter.)
+ *
+ * dk and dv of KV head g sum the contributions of its Hq/Hkv query heads.
+ *
+ *   q, dout        bf16 [B, n*L, Hq, D]
+ *   k, v           bf16 [B, n*L, Hkv, D]
+ *   lse            fp32 [B, Hq, n*L] from sfa_attn_fwd with the same arguments
+ *   dq             bf16 [B, n*L, Hq, D]   written in full
+ *   dk, dv         bf16 [B, n*L, Hkv, D]  written in full
+ *   workspace      device memory of at least sfa_attn_bwd_workspace_size
+ *                  bytes (HD_ERR_WORKSPACE otherwise), owned by the caller,
+ *                  overwritten
+ *   mode           0 within-stream, 1 mixing
+ * Products on bf16 matrix cores with fp32 accumulation; P and dS enter them
+ * as a pair of bf16 halves (hi + lo, about 2^-17 relative), the outputs are
+ * rounded to nearest even.  No atomics: the result is bitwise reproducible.  All pointers 16-byte aligned, D 64 or 128,
+ * Hq a multiple of Hkv.
+ */
+hd_status sfa_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                       const uint16_t* dout, const float* lse,
+                       uint16_t* dq, uint16_t* dk, uint16_t* dv, int64_t B, int32_t n,
+                       int64_t L, int32_t Hq, int32_t Hkv, int32_t D, float softmax_scale,
+                       int32_t mode, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/*
  * sfa_decode_workspace_size -- bytes of device workspace sfa_decode_step
  * needs for these sizes (fp32 split partials).  Returns 0 for invalid sizes.
  */

@@ -16,8 +16,8 @@ import torch
 from ._lib import HDError, check, load  # noqa: F401
 
 __all__ = ["expand", "final_stream_rows", "cyclic_replicate", "stream_attn", "mix_attn",
-           "mix_attn_window", "decode_workspace_size", "decode_step", "HDError", "load",
-           "WITHIN", "MIX"]
+           "mix_attn_window", "attn_fwd", "attn_bwd", "decode_workspace_size", "decode_step",
+           "HDError", "load", "WITHIN", "MIX"]
 
 WITHIN = 0
 MIX = 1
@@ -97,7 +97,7 @@ def cyclic_replicate(tables, n_new: int, out=None):
     return out
 
 
-def _attn(fn_name: str, q, k, v, n: int, scale: float, out, window=None):
+def _attn(fn_name: str, q, k, v, n: int, scale: float, out, window=None, lse=None, mode=None):
     _need(q, "q", torch.bfloat16, 4)
     _need(k, "k", torch.bfloat16, 4)
     _need(v, "v", torch.bfloat16, 4)
@@ -113,8 +113,13 @@ def _attn(fn_name: str, q, k, v, n: int, scale: float, out, window=None):
     if out.shape != q.shape:
         raise ValueError("out must match q")
     extra = () if window is None else (int(window),)
-    st = getattr(load(), fn_name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                  B, n, N // n, Hq, Hkv, D, float(scale), *extra, _stream())
+    if mode is not None:
+        st = getattr(load(), fn_name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                      lse.data_ptr(), B, n, N // n, Hq, Hkv, D, float(scale),
+                                      int(mode), _stream())
+    else:
+        st = getattr(load(), fn_name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                      B, n, N // n, Hq, Hkv, D, float(scale), *extra, _stream())
     check(fn_name, st)
     return out
 
@@ -133,6 +138,56 @@ def mix_attn_window(q, k, v, n: int, scale: float, window: int, out=None):
     """Mixing attention, sliding-window pattern: position i sees keys j with
     i - window < j <= i in the interleaved n*L order (window >= 1)."""
     return _attn("sfa_mix_attn_window", q, k, v, n, scale, out, window)
+
+
+def attn_fwd(q, k, v, n: int, scale: float, mode: int, out=None, lse=None):
+    """Forward of a prefill layer (mode WITHIN or MIX) with its log-sum-exp:
+    returns (out [B, n*L, Hq, D] bf16, lse [B, Hq, n*L] fp32, natural log)."""
+    _need(q, "q", torch.bfloat16, 4)
+    B, N, Hq, _ = q.shape
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _need(lse, "lse", torch.float32, 3)
+    if tuple(lse.shape) != (B, Hq, N):
+        raise ValueError("lse must be [B, Hq, n*L]")
+    out = _attn("sfa_attn_fwd", q, k, v, n, scale, out, lse=lse, mode=mode)
+    return out, lse
+
+
+def attn_bwd(q, k, v, dout, lse, n: int, scale: float, mode: int, dq=None, dk=None,
+             dv=None, workspace=None):
+    """Gradients of a prefill layer: returns (dq, dk, dv) in bf16.  ``lse`` is
+    the forward's (attn_fwd with the same arguments)."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+        _need(t, nm, torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if n < 1 or N % n:
+        raise ValueError(f"sequence length {N} is not a multiple of n={n}")
+    if tuple(k.shape) != (B, N, Hkv, D) or tuple(v.shape) != (B, N, Hkv, D):
+        raise ValueError("k and v must be [B, n*L, Hkv, D] matching q")
+    if tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("dout must match q")
+    if tuple(lse.shape) != (B, Hq, N):
+        raise ValueError("lse must be [B, Hq, n*L]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, nm, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+        _need(t, nm, torch.bfloat16, 4)
+        if t.shape != ref.shape:
+            raise ValueError(f"{nm} must match its input")
+    lib = load()
+    need = int(lib.sfa_attn_bwd_workspace_size(B, n, N // n, Hq))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = lib.sfa_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+                          lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, n, N // n,
+                          Hq, Hkv, D, float(scale), int(mode), workspace.data_ptr(),
+                          workspace.numel() * workspace.element_size(), _stream())
+    check("sfa_attn_bwd", st)
+    return dq, dk, dv
 
 
 def decode_workspace_size(S: int, n: int, Hq: int, Hkv: int, D: int, max_tokens: int) -> int:

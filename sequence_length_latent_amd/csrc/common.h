@@ -58,6 +58,25 @@ __device__ __forceinline__ float halves_sum(float x) {
     return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
+// XOR swizzle of the 16-byte chunks of a row of D bf16 (D/8 chunks) staged in
+// LDS, used for K/V tiles (and Q/dO tiles in the backward kernels).  Two read
+// patterns must hit distinct banks:
+//   direct:    16 consecutive rows, one logical chunk each (16-byte reads);
+//   transpose: per 32 lanes, 4 consecutive rows x 4 consecutive logical
+//              chunks (8-byte ds_read_b64_tr_b16 reads).
+// D=128 (256-byte rows span all 64 banks): swz = (r%4)*4 + (r/4)%4.
+// D=64 (128-byte rows, even/odd rows on opposite bank halves): the same idea
+// over rows of one parity: swz = ((r/2)%2)*4 + (r/4)%4.
+template <int D>
+__device__ __forceinline__ uint32_t swz(uint32_t row) {
+    if constexpr (D == 128) return ((row & 3u) << 2) | ((row >> 2) & 3u);
+    else return (((row >> 1) & 1u) << 2) | ((row >> 2) & 3u);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 inline bool aligned16(const void* p) {
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }

@@ -85,25 +85,9 @@ struct PrefillArgs {
     uint32_t n_items;    // n_qtiles * B * groups * Hkv * n_hpacks
     uint32_t window;     // sliding window W in rows of the view (WIN kernels only)
     float c;             // softmax scale * log2(e)
+    float* lse;          // optional [B, Hq, N] natural log-sum-exp of each row (training)
+    uint32_t Hq, N;
 };
-
-// XOR swizzle of the 16-byte chunks of a K/V row in LDS (rows of D bf16 =
-// D/8 chunks).  Two read patterns must hit distinct banks:
-//   K:  16 consecutive rows, one logical chunk each (16-byte reads);
-//   V:  per 32 lanes, 4 consecutive rows x 4 consecutive logical chunks
-//       (8-byte transpose reads).
-// D=128 (256-byte rows span all 64 banks): swz = (r%4)*4 + (r/4)%4.
-// D=64 (128-byte rows, even/odd rows on opposite bank halves): the same idea
-// over rows of one parity: swz = ((r/2)%2)*4 + (r/4)%4.
-template <int D>
-__device__ __forceinline__ uint32_t swz(uint32_t row) {
-    if constexpr (D == 128) return ((row & 3u) << 2) | ((row >> 2) & 3u);
-    else return (((row >> 1) & 1u) << 2) | ((row >> 2) & 3u);
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
 
 // Scale modes: the exponent argument of a score s is s * c - m with
 // c = softmax scale * log2(e).
@@ -591,6 +575,19 @@ sfa_prefill_kernel(const PrefillArgs a) {
             issue(nx.vview, lo_of(nx), vbuf(0));
         }
         store_out(cur.id, cur.qi);
+        if (a.lse != nullptr && hh == 0 && cur.qi < a.len) {
+            // log-sum-exp of the scaled scores: m and l are in log2 units of c * s
+            uint32_t r = cur.id % per_tile;
+            const uint32_t hp = r % a.n_hpacks;
+            r /= a.n_hpacks;
+            const uint32_t kvh = r % a.Hkv;
+            r /= a.Hkv;
+            const uint32_t grp = r % a.groups;
+            const uint32_t b = r / a.groups;
+            const uint32_t h = kvh * a.G + hp * a.P + (uint32_t)wave % a.P;
+            a.lse[((uint64_t)b * a.Hq + h) * a.N + (uint64_t)cur.qi * a.groups + grp] =
+                (m_run + __builtin_amdgcn_logf(l_run)) * 0.6931471805599453f;
+        }
         if (!more) break;
         cur = make_item(nid);
         ++round;
@@ -614,7 +611,7 @@ int device_cus() {
 hd_status launch_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          uint16_t* out, int64_t B, int32_t n, int64_t L, int32_t Hq,
                          int32_t Hkv, int32_t D, float scale, hipStream_t stream,
-                         bool within, int64_t window) {
+                         bool within, int64_t window, float* lse = nullptr) {
     // window: 0 = none (plain causal), else >= 1 rows of the view
     if (B < 0 || L < 0 || n < 1 || Hq < 1 || Hkv < 1 || window < 0) return HD_ERR_SHAPE;
     if (Hq % Hkv != 0) return HD_ERR_SHAPE;
@@ -647,6 +644,9 @@ hd_status launch_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v
     const uint32_t BT = MQ * (NW / a.P);
     a.n_qtiles = (a.len + BT - 1) / BT;
     a.c = scale * kLog2e;
+    a.lse = lse;
+    a.Hq = (uint32_t)Hq;
+    a.N = (uint32_t)N;
 
     const uint64_t items = (uint64_t)a.n_qtiles * a.B * a.groups * a.Hkv * a.n_hpacks;
     if (items > 0x7fffffffULL) return HD_ERR_UNSUPPORTED;
@@ -692,6 +692,16 @@ extern "C" hd_status sfa_mix_attn(const uint16_t* q, const uint16_t* k,
                                   int32_t D, float softmax_scale, hipStream_t stream) {
     return hdsfa::launch_prefill(q, k, v, out, B, n, L, Hq, Hkv, D, softmax_scale,
                                  stream, /*within=*/false, /*window=*/0);
+}
+
+extern "C" hd_status sfa_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                  uint16_t* out, float* lse, int64_t B, int32_t n, int64_t L,
+                                  int32_t Hq, int32_t Hkv, int32_t D, float softmax_scale,
+                                  int32_t mode, hipStream_t stream) {
+    if (mode != 0 && mode != 1) return HD_ERR_SHAPE;
+    if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return HD_ERR_SHAPE;
+    return hdsfa::launch_prefill(q, k, v, out, B, n, L, Hq, Hkv, D, softmax_scale, stream,
+                                 /*within=*/mode == 0, /*window=*/0, lse);
 }
 
 extern "C" hd_status sfa_mix_attn_window(const uint16_t* q, const uint16_t* k,

@@ -31,8 +31,9 @@ def test_every_declared_symbol_is_exported(lib):
     names = _declared()
     assert set(names) == {"hd_status_string", "hd_abi_version", "hd_expand",
                           "hd_final_stream_rows", "hd_cyclic_replicate", "sfa_stream_attn",
-                          "sfa_mix_attn", "sfa_mix_attn_window", "sfa_decode_workspace_size",
-                          "sfa_decode_step"}
+                          "sfa_mix_attn", "sfa_mix_attn_window", "sfa_attn_fwd",
+                          "sfa_attn_bwd_workspace_size", "sfa_attn_bwd",
+                          "sfa_decode_workspace_size", "sfa_decode_step"}
     for name in names:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, name
@@ -89,6 +90,23 @@ def test_stream_copy_validation(lib):
     assert c(None, 2, 5, 8, FAKE, 4, None) == NULL
     assert c(FAKE, 4, 5, 8, FAKE, 2, None) == OK                   # in place, nothing to add
     assert c(None, 2, 0, 8, None, 4, None) == OK                   # empty tables
+
+
+def test_training_entry_validation(lib):
+    f, b, ws = lib.sfa_attn_fwd, lib.sfa_attn_bwd, lib.sfa_attn_bwd_workspace_size
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 8, 4, 2, 128, 1.0, 2, None) == SHAPE     # mode
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE + 2, 1, 2, 8, 4, 2, 128, 1.0, 1, None) == SHAPE  # lse align
+    assert f(None, FAKE, FAKE, FAKE, None, 1, 2, 8, 4, 2, 128, 1.0, 0, None) == NULL
+    assert f(None, None, None, None, None, 0, 2, 8, 4, 2, 128, 1.0, 0, None) == OK
+    assert ws(2, 4, 1024, 32) == 2 * 32 * 4096 * 4
+    assert ws(-1, 4, 8, 2) == 0
+    args = [FAKE] * 8
+    assert b(*args, 1, 2, 8, 4, 2, 128, 1.0, 3, FAKE, 1 << 20, None) == SHAPE           # mode
+    assert b(*args, 1, 2, 8, 4, 3, 128, 1.0, 0, FAKE, 1 << 20, None) == SHAPE           # Hq % Hkv
+    assert b(*args, 1, 2, 8, 4, 2, 96, 1.0, 0, FAKE, 1 << 20, None) == UNSUP            # D
+    assert b(*args, 1, 2, 8, 4, 2, 128, 1.0, 0, FAKE, 16, None) == WS                   # workspace
+    assert b(None, *args[1:], 1, 2, 8, 4, 2, 128, 1.0, 0, FAKE, 1 << 20, None) == NULL
+    assert b(*args, 0, 2, 8, 4, 2, 128, 1.0, 0, FAKE, 0, None) == OK                    # empty
 
 
 def test_window_validation(lib):

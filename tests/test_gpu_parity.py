@@ -273,6 +273,111 @@ def test_prefill_window_full_size_sampled():
     assert_close(got, ref, f"n4 window {W} sampled")
 
 
+# ---------------------------------------------------------------------------
+# training: forward with log-sum-exp, gradients
+# ---------------------------------------------------------------------------
+def _assert_lse(got, ref, what):
+    err = np.abs(got - ref)
+    assert np.all(err <= 1e-3 + 1e-4 * np.abs(ref)), f"{what}: max lse error {err.max():.3g}"
+
+
+@pytest.mark.parametrize("n,B,L,Hq,Hkv,D,mode", [(2, 1, 70, 4, 2, 128, WITHIN), (3, 2, 33, 8, 2, 64, MIX),
+                                                  (1, 1, 200, 16, 2, 128, MIX), (4, 1, 65, 8, 8, 128, WITHIN)])
+def test_attn_fwd_lse(n, B, L, Hq, Hkv, D, mode):
+    seed = 6000 + 13 * n + L + mode
+    N = n * L
+    q = _rand((B, N, Hq, D), D ** -0.5, seed)
+    k = _rand((B, N, Hkv, D), 1.0, seed + 1)
+    v = _rand((B, N, Hkv, D), 1.0, seed + 2)
+    out, lse = hd.attn_fwd(q, k, v, n, 1.0, mode)
+    plain = FNS[mode](q, k, v, n, 1.0)
+    assert torch.equal(out.view(torch.int16), plain.view(torch.int16))
+    do = torch.zeros_like(q)
+    _, _, _, ref = oracle.prefill_backward_ref(si.bits(q.cpu()), si.bits(k.cpu()), si.bits(v.cpu()),
+                                               si.bits(do.cpu()), n, mode, 1.0)
+    _assert_lse(lse.permute(0, 2, 1).cpu().numpy().astype(np.float64), ref, f"lse n={n} mode={mode}")
+
+
+BWD_SWEEP = [
+    # n, B, L, Hq, Hkv, D, mode
+    (2, 1, 70, 4, 2, 128, WITHIN),
+    (2, 1, 70, 4, 2, 128, MIX),
+    (3, 2, 45, 8, 2, 64, WITHIN),
+    (3, 1, 45, 8, 2, 64, MIX),
+    (4, 1, 129, 8, 1, 128, MIX),       # a partial last key tile of 128
+    (5, 1, 40, 16, 2, 128, WITHIN),    # P = 8 packing
+    (1, 1, 300, 2, 2, 128, MIX),       # P = 1
+]
+
+
+@pytest.mark.parametrize("n,B,L,Hq,Hkv,D,mode", BWD_SWEEP)
+def test_attn_bwd_sweep(n, B, L, Hq, Hkv, D, mode):
+    seed = 6500 + 31 * n + 7 * L + Hq + D + mode
+    N = n * L
+    scale = D ** -0.5
+    q = _rand((B, N, Hq, D), 1.0, seed)
+    k = _rand((B, N, Hkv, D), 1.0, seed + 1)
+    v = _rand((B, N, Hkv, D), 1.0, seed + 2)
+    do = _rand((B, N, Hq, D), 1.0, seed + 3)
+    out, lse = hd.attn_fwd(q, k, v, n, scale, mode)
+    dq, dk, dv = hd.attn_bwd(q, k, v, do, lse, n, scale, mode)
+    rq, rk, rv, _ = oracle.prefill_backward_ref(si.bits(q.cpu()), si.bits(k.cpu()), si.bits(v.cpu()),
+                                                si.bits(do.cpu()), n, mode, scale)
+    what = f"bwd n={n} L={L} H={Hq}/{Hkv} D={D} mode={mode}"
+    assert_close(f64(dq.cpu()), rq, "dq " + what)
+    assert_close(f64(dk.cpu()), rk, "dk " + what)
+    assert_close(f64(dv.cpu()), rv, "dv " + what)
+
+
+def test_attn_bwd_single_position():
+    """One position: P = 1, so dV = dO and dQ = dK = 0 (dS = P (dP - delta)
+    vanishes up to rounding)."""
+    q = _rand((1, 1, 2, 64), 1.0, 6400)
+    k = _rand((1, 1, 1, 64), 1.0, 6401)
+    v = _rand((1, 1, 1, 64), 1.0, 6402)
+    do = _rand((1, 1, 2, 64), 1.0, 6403)
+    out, lse = hd.attn_fwd(q, k, v, 1, 0.125, MIX)
+    dq, dk, dv = hd.attn_bwd(q, k, v, do, lse, 1, 0.125, MIX)
+    # P = 1 up to the rounding of lse (stored in natural-log units): dV equals
+    # the sum of the two heads' dO within one bf16 rounding
+    want = do[:, :, 0].float() + do[:, :, 1].float()
+    assert torch.all((dv[:, :, 0].float() - want).abs() <= want.abs() * 2.0 ** -8 + 1e-6)
+    assert float(dq.float().abs().max()) < 1e-5 and float(dk.float().abs().max()) < 1e-5
+
+
+@pytest.mark.parametrize("mode", [WITHIN, MIX])
+def test_attn_bwd_n4_full_size_one_group(mode):
+    """The n4 workload at full size; the oracle computes batch 0, KV head 0
+    (its four query heads) over every row."""
+    cfg = si.N4
+    q, k, v = si.prefill_qkv(cfg, device=DEV)
+    do = _rand(q.shape, 1.0, 6900 + mode)
+    out, lse = hd.attn_fwd(q, k, v, cfg.n, cfg.scale, mode)
+    dq, dk, dv = hd.attn_bwd(q, k, v, do, lse, cfg.n, cfg.scale, mode)
+    torch.cuda.synchronize()
+    G = cfg.Hq // cfg.Hkv
+    rq, rk, rv, _ = oracle.prefill_backward_ref(si.bits(q[:1].cpu()), si.bits(k[:1].cpu()),
+                                                si.bits(v[:1].cpu()), si.bits(do[:1].cpu()),
+                                                cfg.n, mode, cfg.scale, heads=[0])
+    assert_close(f64(dq[:1, :, :G].cpu()), rq, f"n4 dq mode={mode}")
+    assert_close(f64(dk[:1, :, :1].cpu()), rk, f"n4 dk mode={mode}")
+    assert_close(f64(dv[:1, :, :1].cpu()), rv, f"n4 dv mode={mode}")
+
+
+def test_attn_bwd_deterministic():
+    n, B, L, Hq, Hkv, D = 3, 1, 90, 8, 2, 128
+    N = n * L
+    q = _rand((B, N, Hq, D), 1.0, 6950)
+    k = _rand((B, N, Hkv, D), 1.0, 6951)
+    v = _rand((B, N, Hkv, D), 1.0, 6952)
+    do = _rand((B, N, Hq, D), 1.0, 6953)
+    out, lse = hd.attn_fwd(q, k, v, n, D ** -0.5, MIX)
+    a = hd.attn_bwd(q, k, v, do, lse, n, D ** -0.5, MIX)
+    b = hd.attn_bwd(q, k, v, do, lse, n, D ** -0.5, MIX)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("mode", [WITHIN, MIX])
 def test_prefill_nonunit_scale(D, mode):
