@@ -160,6 +160,27 @@ def bench_prefill(args, torch, hd, si):
     torch.cuda.synchronize()
     t_cr = ew[0].elapsed_time(ew[1]) / reps
     cr_bytes = 2 * (cfg.n - 2) * cfg.vocab * cfg.hidden * 2
+    # training: forward with log-sum-exp, then the gradients, for both layers
+    do = si.randn_bf16(q.shape, 1.0, 0x5FA0F00D, dev)
+    bwd = {}
+    for name, mode in (("within", hd.WITHIN), ("mix", hd.MIX)):
+        o_, lse = hd.attn_fwd(q, k, v, cfg.n, cfg.scale, mode)
+        grads = hd.attn_bwd(q, k, v, do, lse, cfg.n, cfg.scale, mode)
+        torch.cuda.synchronize()
+        reps = max(2, args.steps // 4)
+        ew[0].record()
+        for _ in range(reps):
+            hd.attn_fwd(q, k, v, cfg.n, cfg.scale, mode, out=o_, lse=lse)
+        ew[1].record()
+        torch.cuda.synchronize()
+        t_f = ew[0].elapsed_time(ew[1]) / reps
+        ew[0].record()
+        for _ in range(reps):
+            hd.attn_bwd(q, k, v, do, lse, cfg.n, cfg.scale, mode, *grads)
+        ew[1].record()
+        torch.cuda.synchronize()
+        bwd[name] = (t_f, ew[0].elapsed_time(ew[1]) / reps)
+        del o_, lse, grads
 
     fw = attn_flops(cfg.B, cfg.n, cfg.L, cfg.Hq, cfg.D, "within")
     fm = attn_flops(cfg.B, cfg.n, cfg.L, cfg.Hq, cfg.D, "mix")
@@ -167,7 +188,7 @@ def bench_prefill(args, torch, hd, si):
     exp_bytes = cfg.B * cfg.N * cfg.hidden * 2 * 2 + cfg.B * cfg.L * 4
     res = dict(cfg=cfg, ms_step=ms_step, t_exp=t_exp, t_w=t_w, t_m=t_m, fw=fw, fm=fm,
                exp_bytes=exp_bytes, t_mw=t_mw, fmw=fmw, t_fs=t_fs, fs_bytes=fs_bytes,
-               t_cr=t_cr, cr_bytes=cr_bytes)
+               t_cr=t_cr, cr_bytes=cr_bytes, bwd=bwd)
     del ids, tab, q, k, v, x, ow, om, fsr
     torch.cuda.empty_cache()
     return res
@@ -373,6 +394,14 @@ def main():
                                  "achieved": round(pf["fs_bytes"] / (pf["t_fs"] * 1e-3) / 1e9, 1),
                                  "unit": "GB/s", "peak": PEAK_HBM_GBS,
                                  "note": "[2, 4096, 4096] -> [2, 1024, 4096]; not part of the step"},
+        **{f"sfa_attn_bwd_{name}": {
+            "ms": round(pf["bwd"][name][1], 4), "bound": "mfma",
+            "achieved": round(2.5 * pf[fk] / (pf["bwd"][name][1] * 1e-3) / 1e12, 2),
+            "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS,
+            "fwd_with_lse_ms": round(pf["bwd"][name][0], 4),
+            "note": "gradients dq, dk, dv of the n4 layer; useful work counted as 2.5x the "
+                    "forward's (five products per visible pair); not part of the step"}
+           for name, fk in (("within", "fw"), ("mix", "fm"))},
         "hd_cyclic_replicate": {"ms": round(pf["t_cr"], 4), "bound": "hbm",
                                 "achieved": round(pf["cr_bytes"] / (pf["t_cr"] * 1e-3) / 1e9, 1),
                                 "unit": "GB/s", "peak": PEAK_HBM_GBS,
