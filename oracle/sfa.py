@@ -330,7 +330,7 @@ def decode_append_ref(k_cache, v_cache, k_new, v_new, tokens_before, n):
 
 
 def decode_ref(q_new, k_cache, v_cache, tokens_before, n, mode, scale,
-               seqs=None):
+               seqs=None, window=None):
     """Decode attention for the n new stream positions of one token.
 
     q_new  : bf16 bits [S, n, Hq, D], query of new stream s of sequence q sits
@@ -342,7 +342,8 @@ def decode_ref(q_new, k_cache, v_cache, tokens_before, n, mode, scale,
     The visibility rule is the prefill one restricted to the new queries: the
     within-stream query (T, s) reads entries t'*n + s, t' <= T; the mixing
     query reads every entry up to and including T*n + s (review, *Method*;
-    small-batch decode being bandwidth-bound is the review's *Notes*).
+    small-batch decode being bandwidth-bound is the review's *Notes*).  With
+    ``window`` (mixing only, reading R13) it reads the entries p - W < j <= p.
     """
     q_new = np.asarray(q_new)
     S, _, Hq, D = q_new.shape
@@ -359,7 +360,7 @@ def decode_ref(q_new, k_cache, v_cache, tokens_before, n, mode, scale,
             kf = bf16_bits_to_f64(k_cache[qi, :live, g, :])
             vf = bf16_bits_to_f64(v_cache[qi, :live, g, :])
             qf = bf16_bits_to_f64(q_new[qi, :, h, :])
-            o, _ = attention_rows(qf, pos, kf, vf, n, mode, scale)
+            o, _ = attention_rows(qf, pos, kf, vf, n, mode, scale, window)
             out[si, :, h, :] = o
     return out
 

@@ -511,6 +511,36 @@ def test_decode_append_positions():
                 assert np.array_equal(k2[qi, e], kc[qi, e]) and np.array_equal(v2[qi, e], vc[qi, e])
 
 
+def test_decode_window_equals_windowed_prefill_tail():
+    """With a sliding window the decode rows are the last n rows of the
+    windowed prefill (windows shorter than, equal to and longer than the cache)."""
+    rng = np.random.default_rng(70)
+    S, n, Hq, Hkv, D = 3, 3, 4, 2, 8
+    tb = np.array([0, 5, 2])
+    C = 7 * n
+    kc = _rand_bits(rng, (S, C, Hkv, D))
+    vc = _rand_bits(rng, (S, C, Hkv, D))
+    qn = _rand_bits(rng, (S, n, Hq, D))
+    kn = _rand_bits(rng, (S, n, Hkv, D))
+    vn = _rand_bits(rng, (S, n, Hkv, D))
+    k2, v2 = oracle.decode_append_ref(kc, vc, kn, vn, tb, n)
+    for W in (1, 4, 7, 18, 100):
+        got = oracle.decode_ref(qn, k2, v2, tb, n, MIX, 0.35, window=W)
+        for qi in range(S):
+            T = int(tb[qi])
+            N = (T + 1) * n
+            q = _rand_bits(rng, (1, N, Hq, D))
+            q[0, T * n:] = qn[qi]
+            ref = oracle.prefill_ref(q, k2[qi:qi + 1, :N], v2[qi:qi + 1, :N], n, MIX, 0.35, window=W)
+            np.testing.assert_allclose(got[qi], ref[0, T * n:], rtol=0, atol=1e-13)
+        if W == 1:   # only the query's own (just appended) entry
+            G = Hq // Hkv
+            for qi in range(S):
+                T = int(tb[qi])
+                want = np.repeat(_f(v2[qi, T * n:T * n + n]), G, axis=1)
+                np.testing.assert_allclose(got[qi], want, rtol=0, atol=1e-15)
+
+
 @pytest.mark.parametrize("mode", [WITHIN, MIX])
 def test_decode_equals_prefill_tail(mode):
     """Decoding token T over a cache of T tokens equals the last n rows of a
