@@ -37,6 +37,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
 
 WINDOW = 1024                 # sliding window measured (positions; 256 tokens at n=4)
+DECODE_WINDOW = 4096          # decode sliding window (positions; 1024 tokens at n=4)
 
 
 def pairs(n, L, mode, window=None):
@@ -215,6 +216,19 @@ def bench_decode(args, torch, hd, si):
         e1.record()
         torch.cuda.synchronize()
         res[name] = e0.elapsed_time(e1) / reps
+    # sliding-window mixing decode: the last DECODE_WINDOW + n - 1 entries of each sequence
+    for _ in range(3):
+        hd.decode_step(qn, kn, vn, kc, vc, tb, cfg.n, cfg.T, 1, cfg.scale, ws, out,
+                       window=DECODE_WINDOW)
+    e0, e1 = _events(2)
+    e0.record()
+    for _ in range(reps):
+        hd.decode_step(qn, kn, vn, kc, vc, tb, cfg.n, cfg.T, 1, cfg.scale, ws, out,
+                       window=DECODE_WINDOW)
+    e1.record()
+    torch.cuda.synchronize()
+    res["mix_window"] = e0.elapsed_time(e1) / reps
+    res["bytes_window"] = cfg.S * (DECODE_WINDOW + cfg.n - 1) * cfg.Hkv * cfg.D * 2 * 2
     res["bytes"] = decode_bytes(cfg.S, cfg.n, cfg.T, cfg.Hkv, cfg.D)
     res["cfg"] = cfg
     del qn, kn, vn, kc, vc, tb, ws, out
@@ -452,6 +466,13 @@ def main():
             line["decode"][name] = {"ms": round(dec[name], 4), "achieved": round(gbs, 1),
                                     "unit": "GB/s", "peak": PEAK_HBM_GBS,
                                     "frac": round(gbs / PEAK_HBM_GBS, 4)}
+        gbs = dec["bytes_window"] / (dec["mix_window"] * 1e-3) / 1e9
+        line["decode"]["mix_window"] = {
+            "ms": round(dec["mix_window"], 4), "achieved": round(gbs, 1), "unit": "GB/s",
+            "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4), "window": DECODE_WINDOW,
+            "bytes_per_call": dec["bytes_window"],
+            "note": "sliding-window mixing decode: K+V of the last window + n - 1 entries per "
+                    "sequence; not part of the step"}
         line["decode"]["traffic"] = measured_traffic("decode_attend_kernel", "decode.hip")
     if stack:
         line["stack"] = stack

@@ -271,6 +271,27 @@ hd_status sfa_decode_step(const uint16_t* q_new, const uint16_t* k_new,
                           size_t workspace_bytes, uint16_t* out,
                           hipStream_t stream);
 
+/*
+ * sfa_decode_step_window -- sfa_decode_step for a sliding-window mixing layer
+ * (review, section Method: mixing layers follow the base model's pattern,
+ * sliding-window or full).  After the same append, the new query (T, s) at
+ * p = T*n + s attends to the entries j with p - window < j <= p (window in
+ * interleaved positions, as sfa_mix_attn_window), so only the last
+ * window + n - 1 entries of each sequence are read.
+ *
+ *   window   >= 1 (HD_ERR_SHAPE otherwise); window >= (T+1)*n gives exactly
+ *            the mixing mode of sfa_decode_step
+ * Every other argument, the workspace size and the errors as sfa_decode_step.
+ */
+hd_status sfa_decode_step_window(const uint16_t* q_new, const uint16_t* k_new,
+                                 const uint16_t* v_new, uint16_t* k_cache,
+                                 uint16_t* v_cache, const int32_t* tokens_before,
+                                 int64_t S, int32_t n, int32_t Hq, int32_t Hkv,
+                                 int32_t D, int64_t C_max, int64_t max_tokens,
+                                 int64_t window, float softmax_scale, void* workspace,
+                                 size_t workspace_bytes, uint16_t* out,
+                                 hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -195,10 +195,12 @@ def decode_workspace_size(S: int, n: int, Hq: int, Hkv: int, D: int, max_tokens:
 
 
 def decode_step(q_new, k_new, v_new, k_cache, v_cache, tokens_before, n: int,
-                max_tokens: int, mode: int, scale: float, workspace=None, out=None):
+                max_tokens: int, mode: int, scale: float, workspace=None, out=None,
+                window=None):
     """Append the n new stream positions and attend from them (mode WITHIN or
     MIX).  q_new [S, n, Hq, D]; k_new/v_new [S, n, Hkv, D]; caches
-    [S, C, Hkv, D] (appended in place); tokens_before int32 [S] on the GPU."""
+    [S, C, Hkv, D] (appended in place); tokens_before int32 [S] on the GPU.
+    ``window`` (mode MIX only): sliding window in interleaved positions."""
     _need(q_new, "q_new", torch.bfloat16, 4)
     _need(k_new, "k_new", torch.bfloat16, 4)
     _need(v_new, "v_new", torch.bfloat16, 4)
@@ -224,6 +226,16 @@ def decode_step(q_new, k_new, v_new, k_cache, v_cache, tokens_before, n: int,
     _need(out, "out", torch.bfloat16, 4)
     if out.shape != q_new.shape:
         raise ValueError("out must match q_new")
+    if window is not None:
+        if mode != MIX:
+            raise ValueError("a window applies to the mixing mode only")
+        st = load().sfa_decode_step_window(
+            q_new.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
+            v_cache.data_ptr(), tokens_before.data_ptr(), S, n, Hq, Hkv, D, C, max_tokens,
+            int(window), float(scale), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), out.data_ptr(), _stream())
+        check("sfa_decode_step_window", st)
+        return out
     st = load().sfa_decode_step(q_new.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
                                 k_cache.data_ptr(), v_cache.data_ptr(), tokens_before.data_ptr(),
                                 S, n, Hq, Hkv, D, C, max_tokens, int(mode), float(scale),

@@ -20,6 +20,10 @@
 //                  run on v_mfma_f32_32x32x16_bf16; 4 waves take 32 keys each
 //                  of a 128-key tile and merge their (max, sum, O) at the end;
 //   3. combine  -- merges the per-split partials (fp32) into bf16 output.
+// Sliding-window mixing (sfa_decode_step_window; the review's Method: mixing
+// layers follow the base model's pattern, sliding-window or full): query
+// (T, s) at p = T*n + s reads entries p - W < j <= p, so the view starts at
+// T*n - W + 1 and only W + n - 1 entries per sequence are read.
 // No atomics: results are bitwise reproducible run to run.
 #include "common.h"
 
@@ -44,8 +48,15 @@ struct DecodeArgs {
     uint32_t max_tokens;
     uint32_t nsplit, split;    // splits per view, keys per split (multiple of DT)
     uint32_t within;
+    uint32_t window;           // mixing only: 0 = full pattern, else W
     float c;
 };
+
+// first entry of a view that any of the n new queries can see
+__device__ __forceinline__ uint32_t view_start(uint32_t T, uint32_t n, uint32_t window) {
+    const uint32_t p0 = T * n;
+    return (window != 0u && p0 + 1u >= window) ? p0 + 1u - window : 0u;
+}
 
 __device__ __forceinline__ int vt_pos(int kq) {
     const int qq = kq & 3;
@@ -115,7 +126,8 @@ decode_attend_kernel(const DecodeArgs a) {
 
     const uint32_t T = clamp_tokens(a.tokens_before[seq], a.max_tokens);
     const uint32_t len = a.within ? T + 1 : (T + 1) * a.n;     // keys in the view
-    const uint32_t key0 = sp * a.split;
+    const uint32_t lo = a.within ? 0u : view_start(T, a.n, a.window);
+    const uint32_t key0 = lo + sp * a.split;
     if (key0 >= len) return;                                    // whole block idle
     const uint32_t key_end = min(len, key0 + a.split);
     const int n_tiles = (int)((key_end - key0 + DT - 1) / DT);
@@ -233,12 +245,15 @@ decode_attend_kernel(const DecodeArgs a) {
         bf16x8 pf[NQB][2];
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
-            // keys past the view end or after the query (mixing, new token) -> -inf
-            if (wk0 + 31 > qidx[qb] || wk0 + 31 >= key_end) {
+            // keys past the view end, after the query (mixing, new token) or
+            // before its window -> -inf
+            const bool below = a.window != 0u && wk0 + a.window <= qidx[qb];
+            if (wk0 + 31 > qidx[qb] || wk0 + 31 >= key_end || below) {
 #pragma unroll
                 for (int it = 0; it < 16; ++it) {
                     const uint32_t key = wk0 + 8 * (it >> 2) + 4 * hh + (it & 3);
-                    if (key > qidx[qb] || key >= key_end) sacc[qb][it] = -INFINITY;
+                    if (key > qidx[qb] || key >= key_end || (a.window != 0u && key + a.window <= qidx[qb]))
+                        sacc[qb][it] = -INFINITY;
                 }
             }
             float mx = -INFINITY;
@@ -350,7 +365,7 @@ __global__ void __launch_bounds__(256)
 decode_combine_kernel(const float* __restrict__ ws, const int32_t* __restrict__ tokens_before,
                       uint16_t* __restrict__ out, uint32_t S, uint32_t n, uint32_t Hq,
                       uint32_t Hkv, uint32_t G, uint32_t R, uint32_t nsplit, uint32_t split,
-                      uint32_t within, uint32_t max_tokens) {
+                      uint32_t within, uint32_t max_tokens, uint32_t window) {
     const uint32_t idx = blockIdx.x * 256 + threadIdx.x;    // over S*Hkv*R*D
     if (idx >= S * Hkv * R * D) return;
     const uint32_t d = idx % D;
@@ -361,7 +376,8 @@ decode_combine_kernel(const float* __restrict__ ws, const int32_t* __restrict__ 
     const uint32_t seq = sk / Hkv;
     const uint32_t T = clamp_tokens(tokens_before[seq], max_tokens);
     const uint32_t len = within ? T + 1 : (T + 1) * n;
-    const uint32_t nvalid = (len + split - 1) / split;
+    const uint32_t lo = within ? 0u : view_start(T, n, window);
+    const uint32_t nvalid = (len - lo + split - 1) / split;
     const float* part = ws + (uint64_t)unit * nsplit * (D + 2);
     float M = -INFINITY;
     for (uint32_t sp = 0; sp < nvalid; ++sp) M = fmaxf(M, part[sp * (D + 2)]);
@@ -382,8 +398,10 @@ struct SplitPlan {
     uint32_t nsplit, split;
 };
 
-SplitPlan plan_splits(uint64_t S, uint32_t n, uint32_t Hkv, uint64_t max_tokens, bool within) {
-    const uint64_t len_max = within ? max_tokens + 1 : (max_tokens + 1) * n;
+SplitPlan plan_splits(uint64_t S, uint32_t n, uint32_t Hkv, uint64_t max_tokens, bool within,
+                      uint64_t window = 0) {
+    uint64_t len_max = within ? max_tokens + 1 : (max_tokens + 1) * n;
+    if (!within && window != 0 && window + n - 1 < len_max) len_max = window + n - 1;
     const uint64_t units = S * Hkv * (within ? n : 1u);
     uint64_t want = (kTargetBlocks + units - 1) / units;
     const uint64_t max_splits = (len_max + DT - 1) / DT;
@@ -421,15 +439,13 @@ extern "C" size_t sfa_decode_workspace_size(int64_t S, int32_t n, int32_t Hq, in
     return (size_t)((uint64_t)S * Hkv * R * nsplit * (uint64_t)(D + 2) * sizeof(float));
 }
 
-extern "C" hd_status sfa_decode_step(const uint16_t* q_new, const uint16_t* k_new,
-                                     const uint16_t* v_new, uint16_t* k_cache,
-                                     uint16_t* v_cache, const int32_t* tokens_before,
-                                     int64_t S, int32_t n, int32_t Hq, int32_t Hkv,
-                                     int32_t D, int64_t C_max, int64_t max_tokens,
-                                     int32_t mode, float softmax_scale, void* workspace,
-                                     size_t workspace_bytes, uint16_t* out,
-                                     hipStream_t stream) {
-    using namespace hdsfa;
+namespace hdsfa {
+namespace {
+hd_status decode_step(const uint16_t* q_new, const uint16_t* k_new, const uint16_t* v_new,
+                      uint16_t* k_cache, uint16_t* v_cache, const int32_t* tokens_before,
+                      int64_t S, int32_t n, int32_t Hq, int32_t Hkv, int32_t D, int64_t C_max,
+                      int64_t max_tokens, int32_t mode, float softmax_scale, void* workspace,
+                      size_t workspace_bytes, uint16_t* out, hipStream_t stream, int64_t window) {
     if (S < 0 || n < 1 || Hq < 1 || Hkv < 1 || max_tokens < 0 || C_max < 0) return HD_ERR_SHAPE;
     if (Hq % Hkv != 0) return HD_ERR_SHAPE;
     if (mode != 0 && mode != 1) return HD_ERR_SHAPE;
@@ -466,7 +482,8 @@ extern "C" hd_status sfa_decode_step(const uint16_t* q_new, const uint16_t* k_ne
     }
 
     // 2. attend
-    const SplitPlan plan = plan_splits((uint64_t)S, (uint32_t)n, (uint32_t)Hkv, (uint64_t)max_tokens, within);
+    const SplitPlan plan = plan_splits((uint64_t)S, (uint32_t)n, (uint32_t)Hkv, (uint64_t)max_tokens, within,
+                                       within ? 0u : (uint64_t)window);
     // the workspace stride uses the larger plan of the two modes
     const SplitPlan pw = plan_splits((uint64_t)S, (uint32_t)n, (uint32_t)Hkv, (uint64_t)max_tokens, true);
     const SplitPlan pm = plan_splits((uint64_t)S, (uint32_t)n, (uint32_t)Hkv, (uint64_t)max_tokens, false);
@@ -488,6 +505,7 @@ extern "C" hd_status sfa_decode_step(const uint16_t* q_new, const uint16_t* k_ne
     a.nsplit = ws_nsplit;
     a.split = plan.split;
     a.within = within ? 1u : 0u;
+    a.window = within ? 0u : (uint32_t)window;
     a.c = softmax_scale * kLog2e;
     const uint32_t rows = within ? G : R;
     const dim3 grid(plan.nsplit, (uint32_t)Hkv * (within ? (uint32_t)n : 1u), (uint32_t)S);
@@ -508,10 +526,39 @@ extern "C" hd_status sfa_decode_step(const uint16_t* q_new, const uint16_t* k_ne
     if (D == 128)
         decode_combine_kernel<128><<<dim3(blocks), dim3(256), 0, stream>>>(
             a.ws, tokens_before, out, (uint32_t)S, (uint32_t)n, (uint32_t)Hq, (uint32_t)Hkv, G, R,
-            ws_nsplit, plan.split, a.within, (uint32_t)max_tokens);
+            ws_nsplit, plan.split, a.within, (uint32_t)max_tokens, a.window);
     else
         decode_combine_kernel<64><<<dim3(blocks), dim3(256), 0, stream>>>(
             a.ws, tokens_before, out, (uint32_t)S, (uint32_t)n, (uint32_t)Hq, (uint32_t)Hkv, G, R,
-            ws_nsplit, plan.split, a.within, (uint32_t)max_tokens);
+            ws_nsplit, plan.split, a.within, (uint32_t)max_tokens, a.window);
     return launch_status();
+}
+}  // namespace
+}  // namespace hdsfa
+
+extern "C" hd_status sfa_decode_step(const uint16_t* q_new, const uint16_t* k_new,
+                                     const uint16_t* v_new, uint16_t* k_cache,
+                                     uint16_t* v_cache, const int32_t* tokens_before,
+                                     int64_t S, int32_t n, int32_t Hq, int32_t Hkv,
+                                     int32_t D, int64_t C_max, int64_t max_tokens,
+                                     int32_t mode, float softmax_scale, void* workspace,
+                                     size_t workspace_bytes, uint16_t* out,
+                                     hipStream_t stream) {
+    return hdsfa::decode_step(q_new, k_new, v_new, k_cache, v_cache, tokens_before, S, n, Hq, Hkv, D,
+                              C_max, max_tokens, mode, softmax_scale, workspace, workspace_bytes, out,
+                              stream, 0);
+}
+
+extern "C" hd_status sfa_decode_step_window(const uint16_t* q_new, const uint16_t* k_new,
+                                            const uint16_t* v_new, uint16_t* k_cache,
+                                            uint16_t* v_cache, const int32_t* tokens_before,
+                                            int64_t S, int32_t n, int32_t Hq, int32_t Hkv,
+                                            int32_t D, int64_t C_max, int64_t max_tokens,
+                                            int64_t window, float softmax_scale, void* workspace,
+                                            size_t workspace_bytes, uint16_t* out,
+                                            hipStream_t stream) {
+    if (window < 1 || window > 0x7fffffffLL) return HD_ERR_SHAPE;
+    return hdsfa::decode_step(q_new, k_new, v_new, k_cache, v_cache, tokens_before, S, n, Hq, Hkv, D,
+                              C_max, max_tokens, 1, softmax_scale, workspace, workspace_bytes, out,
+                              stream, window);
 }

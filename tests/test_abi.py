@@ -33,7 +33,8 @@ def test_every_declared_symbol_is_exported(lib):
                           "hd_final_stream_rows", "hd_cyclic_replicate", "sfa_stream_attn",
                           "sfa_mix_attn", "sfa_mix_attn_window", "sfa_attn_fwd",
                           "sfa_attn_bwd_workspace_size", "sfa_attn_bwd",
-                          "sfa_decode_workspace_size", "sfa_decode_step"}
+                          "sfa_decode_workspace_size", "sfa_decode_step",
+                          "sfa_decode_step_window"}
     for name in names:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, name
@@ -149,6 +150,19 @@ def test_decode_validation(lib):
     assert call(ws=None) == WS
     assert call(wsb=16) == WS
     assert call(S=0, q=None) == OK
+
+
+def test_decode_window_validation(lib):
+    def call(window, C=4 * 11, ws=FAKE, wsb=1 << 30, q=FAKE, S=2):
+        return lib.sfa_decode_step_window(q, FAKE, FAKE, FAKE, FAKE, FAKE, S, 4, 8, 2, 128, C, 10,
+                                          window, 0.1, ws, wsb, FAKE, None)
+
+    assert call(0) == SHAPE
+    assert call(-3) == SHAPE
+    assert call(16, q=None) == NULL
+    assert call(16, C=4 * 11 - 1) == CAP
+    assert call(16, wsb=16) == WS
+    assert call(16, S=0, q=None) == OK
 
 
 def test_binding_rejects_host_tensors():

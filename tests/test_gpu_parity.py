@@ -541,11 +541,11 @@ def test_determinism():
 # ---------------------------------------------------------------------------
 # decode
 # ---------------------------------------------------------------------------
-def _decode_case(cfg, S, T, tb, mode, seqs=None, max_tokens=None, device=DEV):
+def _decode_case(cfg, S, T, tb, mode, seqs=None, max_tokens=None, device=DEV, window=None):
     qn, kn, vn, kc, vc, tbt = si.decode_inputs(cfg, device=device, S=S, T=T, tokens_before=tb)
     max_tokens = T if max_tokens is None else max_tokens
     kc0, vc0 = kc.clone(), vc.clone()
-    out = hd.decode_step(qn, kn, vn, kc, vc, tbt, cfg.n, max_tokens, mode, cfg.scale)
+    out = hd.decode_step(qn, kn, vn, kc, vc, tbt, cfg.n, max_tokens, mode, cfg.scale, window=window)
     torch.cuda.synchronize()
     seqs = list(range(S)) if seqs is None else seqs
     tbh = tbt.cpu().numpy()
@@ -555,8 +555,9 @@ def _decode_case(cfg, S, T, tb, mode, seqs=None, max_tokens=None, device=DEV):
                                           si.bits(vn[sl]), tbh[sl], cfg.n)
         assert np.array_equal(si.bits(kc[sl]), k2), f"k append seq {qi}"
         assert np.array_equal(si.bits(vc[sl]), v2), f"v append seq {qi}"
-        ref = oracle.decode_ref(si.bits(qn[sl]), k2, v2, tbh[sl], cfg.n, mode, cfg.scale)
-        assert_close(f64(out[sl]), ref, f"decode seq {qi} T={tbh[qi]} mode={mode}")
+        ref = oracle.decode_ref(si.bits(qn[sl]), k2, v2, tbh[sl], cfg.n, mode, cfg.scale,
+                                window=window)
+        assert_close(f64(out[sl]), ref, f"decode seq {qi} T={tbh[qi]} mode={mode} window={window}")
     return out
 
 
@@ -580,6 +581,36 @@ def test_decode_full_size_sampled(mode):
     """Decode workload at full size: 64 sequences x 16384 cached entries."""
     cfg = si.DECODE
     _decode_case(cfg, S=cfg.S, T=cfg.T, tb=None, mode=mode, seqs=[0, 31, 63])
+
+
+@pytest.mark.parametrize("window", [1, 3, 64, 129, 500, 1 << 20])
+def test_decode_window_ragged(window):
+    """Sliding-window mixing decode over ragged caches (windows inside one
+    token's streams, one tile, past a tile edge, longer than some caches)."""
+    _decode_case(si.DECODE, S=5, T=300, tb=[300, 0, 1, 129, 255], mode=MIX, window=window)
+
+
+def test_decode_window_other_shapes():
+    cfg = si.DecodeCfg("d3w", 12, S=3, n=3, T=200, Hq=16, Hkv=2, D=64, scale=0.125)
+    _decode_case(cfg, S=3, T=200, tb=[200, 77, 3], mode=MIX, window=50)
+    cfg = si.DecodeCfg("d8w", 13, S=2, n=8, T=70, Hq=8, Hkv=1, D=128, scale=0.09)
+    _decode_case(cfg, S=2, T=70, tb=[70, 31], mode=MIX, window=130)
+
+
+def test_decode_window_full_size_sampled():
+    """The decode workload (64 sequences x 16384 entries) with a window of
+    4096 positions (1024 tokens x 4 streams)."""
+    cfg = si.DECODE
+    _decode_case(cfg, S=cfg.S, T=cfg.T, tb=None, mode=MIX, seqs=[0, 31, 63], window=4096)
+
+
+def test_decode_window_long_equals_mix_bitwise():
+    cfg = si.DECODE
+    S, T = 3, 90
+    qn, kn, vn, kc, vc, tb = si.decode_inputs(cfg, device=DEV, S=S, T=T, tokens_before=[90, 4, 50])
+    a = hd.decode_step(qn, kn, vn, kc, vc, tb, cfg.n, T, MIX, cfg.scale)
+    b = hd.decode_step(qn, kn, vn, kc, vc, tb, cfg.n, T, MIX, cfg.scale, window=(T + 1) * cfg.n)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
 def test_decode_idempotent_append_and_modes_share_cache():
