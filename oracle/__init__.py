@@ -16,8 +16,10 @@ from .sfa import (  # noqa: F401
     expand_ref,
     expanded_position,
     final_stream_rows_ref,
+    gather_pages_ref,
     prefill_backward_ref,
     prefill_ref,
+    scatter_pages_ref,
     useful_flops,
     visible,
 )

@@ -329,6 +329,33 @@ def decode_append_ref(k_cache, v_cache, k_new, v_new, tokens_before, n):
     return kc, vc
 
 
+def gather_pages_ref(pool, page_table, entries):
+    """Contiguous cache rows [S, entries, ...] from a paged pool: entry e of
+    sequence q lives in page page_table[q, e // P], slot e % P, with P the
+    page size (pool [num_pages, P, ...]).  Serving stacks keep the retained
+    KV in such pages; the review's *Limitations* count the cache's size, not
+    its layout, so paging is a storage choice that leaves every decode value
+    unchanged."""
+    pool = np.asarray(pool)
+    pt = np.asarray(page_table)
+    P = pool.shape[1]
+    S = pt.shape[0]
+    out = np.zeros((S, entries) + pool.shape[2:], dtype=pool.dtype)
+    for q in range(S):
+        for e in range(entries):
+            out[q, e] = pool[pt[q, e // P], e % P]
+    return out
+
+
+def scatter_pages_ref(pool, page_table, q, e, row):
+    """The inverse placement for one row: a copy of ``pool`` with entry e of
+    sequence q set to ``row``."""
+    pool = np.array(pool, copy=True)
+    P = pool.shape[1]
+    pool[int(page_table[q, e // P]), e % P] = row
+    return pool
+
+
 def decode_ref(q_new, k_cache, v_cache, tokens_before, n, mode, scale,
                seqs=None, window=None):
     """Decode attention for the n new stream positions of one token.

@@ -511,6 +511,20 @@ def test_decode_append_positions():
                 assert np.array_equal(k2[qi, e], kc[qi, e]) and np.array_equal(v2[qi, e], vc[qi, e])
 
 
+def test_page_gather_and_scatter():
+    """Hand-placed pages: page size 2, sequence 0 on pages [3, 0], sequence 1
+    on [1, 2]; entry e of sequence q is pool[pt[q, e // 2], e % 2]."""
+    pool = np.arange(4 * 2 * 3).reshape(4, 2, 3)          # 4 pages x 2 slots x 3 values
+    pt = np.array([[3, 0], [1, 2]])
+    g = oracle.gather_pages_ref(pool, pt, 4)
+    assert np.array_equal(g[0], np.stack([pool[3, 0], pool[3, 1], pool[0, 0], pool[0, 1]]))
+    assert np.array_equal(g[1], np.stack([pool[1, 0], pool[1, 1], pool[2, 0], pool[2, 1]]))
+    assert int(g[0, 2, 0]) == 0 and int(g[1, 3, 2]) == 17     # values computed by hand
+    p2 = oracle.scatter_pages_ref(pool, pt, 1, 2, np.array([-1, -2, -3]))
+    assert np.array_equal(p2[2, 0], [-1, -2, -3]) and np.array_equal(np.delete(p2.reshape(-1, 3), 4, 0),
+                                                                     np.delete(pool.reshape(-1, 3), 4, 0))
+
+
 def test_decode_window_equals_windowed_prefill_tail():
     """With a sliding window the decode rows are the last n rows of the
     windowed prefill (windows shorter than, equal to and longer than the cache)."""
