@@ -272,6 +272,39 @@ hd_status sfa_decode_step(const uint16_t* q_new, const uint16_t* k_new,
                           hipStream_t stream);
 
 /*
+ * sfa_decode_step_paged -- sfa_decode_step over a paged cache (the retained
+ * KV of many sequences of different lengths held in fixed-size pages, as a
+ * serving engine keeps it; review, section Limitations: the enlarged per-
+ * stream cache is what decode pays for).  Entry e of sequence q (e = t*n + s)
+ * lives in page page_table[q, e / page_size], slot e % page_size.
+ *
+ *   k_pages, v_pages  bf16 [num_pages, page_size, Hkv, D] pools
+ *   page_table        int32 [S, max_pages_per_seq], device memory; ids outside
+ *                     [0, num_pages) are clamped into it on the device (no
+ *                     access leaves the pool)
+ *   page_size         a power of two (HD_ERR_SHAPE otherwise)
+ *   max_tokens        as sfa_decode_step; (max_tokens+1)*n must fit in
+ *                     max_pages_per_seq*page_size entries (HD_ERR_CAPACITY)
+ *   mode              0 within-stream, 1 mixing
+ *   window            0 for the full pattern, or the sliding window of a
+ *                     mixing layer (as sfa_decode_step_window; HD_ERR_SHAPE
+ *                     with mode 0)
+ * The append writes the new rows into their pages; the attention reads every
+ * live row through the table.  The result equals sfa_decode_step (or
+ * sfa_decode_step_window) on the same rows laid out contiguously, bit for
+ * bit.  Workspace size as sfa_decode_workspace_size(S, n, Hq, Hkv, D,
+ * max_tokens).
+ */
+hd_status sfa_decode_step_paged(const uint16_t* q_new, const uint16_t* k_new,
+                                const uint16_t* v_new, uint16_t* k_pages, uint16_t* v_pages,
+                                const int32_t* page_table, const int32_t* tokens_before,
+                                int64_t S, int32_t n, int32_t Hq, int32_t Hkv, int32_t D,
+                                int32_t page_size, int64_t num_pages, int32_t max_pages_per_seq,
+                                int64_t max_tokens, int32_t mode, int64_t window,
+                                float softmax_scale, void* workspace, size_t workspace_bytes,
+                                uint16_t* out, hipStream_t stream);
+
+/*
  * sfa_decode_step_window -- sfa_decode_step for a sliding-window mixing layer
  * (review, section Method: mixing layers follow the base model's pattern,
  * sliding-window or full).  After the same append, the new query (T, s) at

@@ -17,6 +17,7 @@ from ._lib import HDError, check, load  # noqa: F401
 
 __all__ = ["expand", "final_stream_rows", "cyclic_replicate", "stream_attn", "mix_attn",
            "mix_attn_window", "attn_fwd", "attn_bwd", "decode_workspace_size", "decode_step",
+           "decode_step_paged",
            "HDError", "load", "WITHIN", "MIX"]
 
 WITHIN = 0
@@ -242,4 +243,42 @@ def decode_step(q_new, k_new, v_new, k_cache, v_cache, tokens_before, n: int,
                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                 out.data_ptr(), _stream())
     check("sfa_decode_step", st)
+    return out
+
+
+def decode_step_paged(q_new, k_new, v_new, k_pages, v_pages, page_table, tokens_before, n: int,
+                      max_tokens: int, mode: int, scale: float, window=None, workspace=None,
+                      out=None):
+    """decode_step over paged caches: pools [num_pages, P, Hkv, D] (appended in
+    place), page_table int32 [S, max_pages_per_seq] and tokens_before int32 [S]
+    on the GPU.  ``window`` (mode MIX only): sliding window in positions."""
+    for t, nm in ((q_new, "q_new"), (k_new, "k_new"), (v_new, "v_new"), (k_pages, "k_pages"),
+                  (v_pages, "v_pages")):
+        _need(t, nm, torch.bfloat16, 4)
+    _need(page_table, "page_table", torch.int32, 2)
+    _need(tokens_before, "tokens_before", torch.int32, 1)
+    S, n_, Hq, D = q_new.shape
+    if n_ != n:
+        raise ValueError("q_new must be [S, n, Hq, D]")
+    Hkv = k_new.shape[2]
+    num_pages, P = k_pages.shape[0], k_pages.shape[1]
+    if tuple(k_new.shape) != (S, n, Hkv, D) or tuple(v_new.shape) != (S, n, Hkv, D):
+        raise ValueError("k_new/v_new must be [S, n, Hkv, D]")
+    if tuple(k_pages.shape) != (num_pages, P, Hkv, D) or tuple(v_pages.shape) != tuple(k_pages.shape):
+        raise ValueError("page pools must be [num_pages, page_size, Hkv, D]")
+    if page_table.shape[0] != S or tuple(tokens_before.shape) != (S,):
+        raise ValueError("page_table must be [S, max_pages] and tokens_before [S]")
+    need = decode_workspace_size(S, n, Hq, Hkv, D, max_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_new.device)
+    if out is None:
+        out = torch.empty_like(q_new)
+    _need(out, "out", torch.bfloat16, 4)
+    st = load().sfa_decode_step_paged(
+        q_new.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+        page_table.data_ptr(), tokens_before.data_ptr(), S, n, Hq, Hkv, D, P, num_pages,
+        page_table.shape[1], max_tokens, int(mode), 0 if window is None else int(window),
+        float(scale), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        out.data_ptr(), _stream())
+    check("sfa_decode_step_paged", st)
     return out

@@ -24,6 +24,9 @@
 // layers follow the base model's pattern, sliding-window or full): query
 // (T, s) at p = T*n + s reads entries p - W < j <= p, so the view starts at
 // T*n - W + 1 and only W + n - 1 entries per sequence are read.
+// Paged caches (sfa_decode_step_paged): entry e of sequence q lives in page
+// page_table[q, e / P], slot e % P (P a power of two) of a pool of pages; the
+// same kernels look every cache row up through the table (PAGED instances).
 // No atomics: results are bitwise reproducible run to run.
 #include "common.h"
 
@@ -50,7 +53,19 @@ struct DecodeArgs {
     uint32_t within;
     uint32_t window;           // mixing only: 0 = full pattern, else W
     float c;
+    const int32_t* page_table; // [S, mpps] (PAGED instances)
+    uint32_t pshift, mpps, num_pages;
 };
+
+// pool row of entry e of sequence seq (page ids outside the pool are clamped
+// into it, so no access leaves the pool)
+__device__ __forceinline__ uint64_t paged_row(const int32_t* __restrict__ pt, uint32_t seq, uint32_t e,
+                                              uint32_t pshift, uint32_t mpps, uint32_t num_pages) {
+    const uint32_t slot = min(e >> pshift, mpps - 1u);
+    int32_t pg = pt[(uint64_t)seq * mpps + slot];
+    pg = pg < 0 ? 0 : (pg >= (int32_t)num_pages ? (int32_t)num_pages - 1 : pg);
+    return ((uint64_t)(uint32_t)pg << pshift) | (e & ((1u << pshift) - 1u));
+}
 
 // first entry of a view that any of the n new queries can see
 __device__ __forceinline__ uint32_t view_start(uint32_t T, uint32_t n, uint32_t window) {
@@ -70,19 +85,27 @@ __device__ __forceinline__ uint32_t clamp_tokens(int32_t t, uint32_t max_tokens)
 // ---------------------------------------------------------------------------
 // 1. append
 // ---------------------------------------------------------------------------
+template <bool PAGED>
 __global__ void __launch_bounds__(256)
 decode_append_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ v_new,
                      u32x4* __restrict__ kc, u32x4* __restrict__ vc,
                      const int32_t* __restrict__ tokens_before, uint32_t S, uint32_t n,
                      uint32_t row_chunks /* Hkv*D/8 */, uint64_t cache_seq_chunks,
-                     uint32_t max_tokens) {
+                     uint32_t max_tokens, const int32_t* __restrict__ pt, uint32_t pshift,
+                     uint32_t mpps, uint32_t num_pages) {
     const uint32_t idx = blockIdx.x * 256 + threadIdx.x;
     const uint32_t per_seq = n * row_chunks;
     if (idx >= S * per_seq) return;
     const uint32_t seq = idx / per_seq;
     const uint32_t rem = idx - seq * per_seq;      // s*row_chunks + w
     const uint32_t T = clamp_tokens(tokens_before[seq], max_tokens);
-    const uint64_t dst = seq * cache_seq_chunks + (uint64_t)T * n * row_chunks + rem;
+    uint64_t dst;
+    if constexpr (PAGED) {
+        const uint32_t s = rem / row_chunks;
+        dst = paged_row(pt, seq, T * n + s, pshift, mpps, num_pages) * row_chunks + (rem - s * row_chunks);
+    } else {
+        dst = seq * cache_seq_chunks + (uint64_t)T * n * row_chunks + rem;
+    }
     kc[dst] = k_new[idx];
     vc[dst] = v_new[idx];
 }
@@ -90,7 +113,7 @@ decode_append_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ 
 // ---------------------------------------------------------------------------
 // 2. split-K attention
 // ---------------------------------------------------------------------------
-template <int D, int NQB>
+template <int D, int NQB, bool PAGED>
 __global__ void __launch_bounds__(DTHREADS) __attribute__((amdgpu_waves_per_eu(1, 2)))
 decode_attend_kernel(const DecodeArgs a) {
     constexpr int KP = D + 8;
@@ -186,7 +209,12 @@ decode_attend_kernel(const DecodeArgs a) {
         for (int i = 0; i < K_CHUNKS; ++i) {
             const int cidx = tid + i * DTHREADS;
             const uint32_t key = min(k0 + cidx / CPR, last_key);
-            r.k[i] = *reinterpret_cast<const u32x4*>(kbase + key * kstep + (cidx % CPR) * 8);
+            if constexpr (PAGED) {
+                const uint64_t row = paged_row(a.page_table, seq, key * rstride + view, a.pshift, a.mpps, a.num_pages);
+                r.k[i] = *reinterpret_cast<const u32x4*>(a.kc + row * erow + (uint64_t)kvh * D + (cidx % CPR) * 8);
+            } else {
+                r.k[i] = *reinterpret_cast<const u32x4*>(kbase + key * kstep + (cidx % CPR) * 8);
+            }
         }
 #pragma unroll
         for (int i = 0; i < V_PER; ++i) {
@@ -196,7 +224,13 @@ decode_attend_kernel(const DecodeArgs a) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const uint32_t key = min(k0 + 4 * kq + q, last_key);
-                r.v[i][q] = *reinterpret_cast<const u32x4*>(vbase + key * kstep + dq * 8);
+                if constexpr (PAGED) {
+                    const uint64_t row = paged_row(a.page_table, seq, key * rstride + view, a.pshift, a.mpps,
+                                                   a.num_pages);
+                    r.v[i][q] = *reinterpret_cast<const u32x4*>(a.vc + row * erow + (uint64_t)kvh * D + dq * 8);
+                } else {
+                    r.v[i][q] = *reinterpret_cast<const u32x4*>(vbase + key * kstep + dq * 8);
+                }
             }
         }
     };
@@ -441,11 +475,18 @@ extern "C" size_t sfa_decode_workspace_size(int64_t S, int32_t n, int32_t Hq, in
 
 namespace hdsfa {
 namespace {
+struct Paging {
+    const int32_t* page_table = nullptr;   // nullptr: contiguous [S, C_max, Hkv, D] caches
+    uint32_t pshift = 0, mpps = 0, num_pages = 0;
+};
+
 hd_status decode_step(const uint16_t* q_new, const uint16_t* k_new, const uint16_t* v_new,
                       uint16_t* k_cache, uint16_t* v_cache, const int32_t* tokens_before,
                       int64_t S, int32_t n, int32_t Hq, int32_t Hkv, int32_t D, int64_t C_max,
                       int64_t max_tokens, int32_t mode, float softmax_scale, void* workspace,
-                      size_t workspace_bytes, uint16_t* out, hipStream_t stream, int64_t window) {
+                      size_t workspace_bytes, uint16_t* out, hipStream_t stream, int64_t window,
+                      const Paging& pg = Paging{}) {
+    const bool paged = pg.page_table != nullptr;
     if (S < 0 || n < 1 || Hq < 1 || Hkv < 1 || max_tokens < 0 || C_max < 0) return HD_ERR_SHAPE;
     if (Hq % Hkv != 0) return HD_ERR_SHAPE;
     if (mode != 0 && mode != 1) return HD_ERR_SHAPE;
@@ -472,11 +513,12 @@ hd_status decode_step(const uint16_t* q_new, const uint16_t* k_new, const uint16
         const uint64_t total = (uint64_t)S * n * row_chunks;
         if (total > 0x7fffffffULL) return HD_ERR_UNSUPPORTED;
         const uint32_t blocks = (uint32_t)((total + 255) / 256);
-        decode_append_kernel<<<dim3(blocks), dim3(256), 0, stream>>>(
+        (paged ? decode_append_kernel<true> : decode_append_kernel<false>)
+            <<<dim3(blocks), dim3(256), 0, stream>>>(
             reinterpret_cast<const u32x4*>(k_new), reinterpret_cast<const u32x4*>(v_new),
             reinterpret_cast<u32x4*>(k_cache), reinterpret_cast<u32x4*>(v_cache),
             tokens_before, (uint32_t)S, (uint32_t)n, row_chunks, cache_seq / 8,
-            (uint32_t)max_tokens);
+            (uint32_t)max_tokens, pg.page_table, pg.pshift, pg.mpps, pg.num_pages);
         const hd_status st = launch_status();
         if (st != HD_OK) return st;
     }
@@ -507,14 +549,22 @@ hd_status decode_step(const uint16_t* q_new, const uint16_t* k_new, const uint16
     a.within = within ? 1u : 0u;
     a.window = within ? 0u : (uint32_t)window;
     a.c = softmax_scale * kLog2e;
+    a.page_table = pg.page_table;
+    a.pshift = pg.pshift;
+    a.mpps = pg.mpps;
+    a.num_pages = pg.num_pages;
     const uint32_t rows = within ? G : R;
     const dim3 grid(plan.nsplit, (uint32_t)Hkv * (within ? (uint32_t)n : 1u), (uint32_t)S);
     if (D == 128) {
-        if (rows <= 32) decode_attend_kernel<128, 1><<<grid, dim3(DTHREADS), 0, stream>>>(a);
-        else            decode_attend_kernel<128, 2><<<grid, dim3(DTHREADS), 0, stream>>>(a);
+        if (rows <= 32) (paged ? decode_attend_kernel<128, 1, true> : decode_attend_kernel<128, 1, false>)
+                            <<<grid, dim3(DTHREADS), 0, stream>>>(a);
+        else            (paged ? decode_attend_kernel<128, 2, true> : decode_attend_kernel<128, 2, false>)
+                            <<<grid, dim3(DTHREADS), 0, stream>>>(a);
     } else {
-        if (rows <= 32) decode_attend_kernel<64, 1><<<grid, dim3(DTHREADS), 0, stream>>>(a);
-        else            decode_attend_kernel<64, 2><<<grid, dim3(DTHREADS), 0, stream>>>(a);
+        if (rows <= 32) (paged ? decode_attend_kernel<64, 1, true> : decode_attend_kernel<64, 1, false>)
+                            <<<grid, dim3(DTHREADS), 0, stream>>>(a);
+        else            (paged ? decode_attend_kernel<64, 2, true> : decode_attend_kernel<64, 2, false>)
+                            <<<grid, dim3(DTHREADS), 0, stream>>>(a);
     }
     hd_status st = launch_status();
     if (st != HD_OK) return st;
@@ -547,6 +597,34 @@ extern "C" hd_status sfa_decode_step(const uint16_t* q_new, const uint16_t* k_ne
     return hdsfa::decode_step(q_new, k_new, v_new, k_cache, v_cache, tokens_before, S, n, Hq, Hkv, D,
                               C_max, max_tokens, mode, softmax_scale, workspace, workspace_bytes, out,
                               stream, 0);
+}
+
+extern "C" hd_status sfa_decode_step_paged(const uint16_t* q_new, const uint16_t* k_new,
+                                           const uint16_t* v_new, uint16_t* k_pages,
+                                           uint16_t* v_pages, const int32_t* page_table,
+                                           const int32_t* tokens_before, int64_t S, int32_t n,
+                                           int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size,
+                                           int64_t num_pages, int32_t max_pages_per_seq,
+                                           int64_t max_tokens, int32_t mode, int64_t window,
+                                           float softmax_scale, void* workspace,
+                                           size_t workspace_bytes, uint16_t* out,
+                                           hipStream_t stream) {
+    using namespace hdsfa;
+    if (page_size < 1 || (page_size & (page_size - 1)) != 0) return HD_ERR_SHAPE;
+    if (num_pages < 1 || num_pages > 0x7fffffffLL || max_pages_per_seq < 1) return HD_ERR_SHAPE;
+    if (window < 0 || (window > 0 && mode != 1) || window > 0x7fffffffLL) return HD_ERR_SHAPE;
+    if (S > 0 && page_table == nullptr) return HD_ERR_NULL;
+    // row indices within the pool fit 32 bits + the page shift in 64-bit math
+    Paging pg;
+    pg.page_table = page_table;
+    pg.pshift = (uint32_t)__builtin_ctz((unsigned)page_size);
+    pg.mpps = (uint32_t)max_pages_per_seq;
+    pg.num_pages = (uint32_t)num_pages;
+    const int64_t capacity = (int64_t)max_pages_per_seq * page_size;   // entries a sequence can hold
+    if (S == 0) pg.page_table = nullptr;
+    return decode_step(q_new, k_new, v_new, k_pages, v_pages, tokens_before, S, n, Hq, Hkv, D,
+                       capacity, max_tokens, mode, softmax_scale, workspace, workspace_bytes, out,
+                       stream, window, pg);
 }
 
 extern "C" hd_status sfa_decode_step_window(const uint16_t* q_new, const uint16_t* k_new,

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(lib):
                           "sfa_mix_attn", "sfa_mix_attn_window", "sfa_attn_fwd",
                           "sfa_attn_bwd_workspace_size", "sfa_attn_bwd",
                           "sfa_decode_workspace_size", "sfa_decode_step",
-                          "sfa_decode_step_window"}
+                          "sfa_decode_step_window", "sfa_decode_step_paged"}
     for name in names:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, name
@@ -163,6 +163,22 @@ def test_decode_window_validation(lib):
     assert call(16, C=4 * 11 - 1) == CAP
     assert call(16, wsb=16) == WS
     assert call(16, S=0, q=None) == OK
+
+
+def test_decode_paged_validation(lib):
+    def call(P=16, num_pages=64, mpps=8, mode=1, window=0, C=None, pt=FAKE, q=FAKE, S=2, wsb=1 << 30):
+        return lib.sfa_decode_step_paged(q, FAKE, FAKE, FAKE, FAKE, pt, FAKE, S, 4, 8, 2, 128, P,
+                                         num_pages, mpps, 10, mode, window, 0.1, FAKE, wsb, FAKE, None)
+
+    assert call(P=12) == SHAPE                  # not a power of two
+    assert call(P=0) == SHAPE
+    assert call(num_pages=0) == SHAPE
+    assert call(mode=0, window=8) == SHAPE      # window on a within-stream layer
+    assert call(window=-1) == SHAPE
+    assert call(mpps=2) == CAP                  # 2 pages x 16 < 11 tokens x 4 streams
+    assert call(pt=None) == NULL
+    assert call(wsb=16) == WS
+    assert call(S=0, q=None, pt=None) == OK
 
 
 def test_binding_rejects_host_tensors():

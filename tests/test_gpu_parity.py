@@ -613,6 +613,64 @@ def test_decode_window_long_equals_mix_bitwise():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+def _paged_from(kc, vc, P, seed, spare=3):
+    """A page pool holding the contiguous caches' rows in shuffled pages (plus
+    spare pages filled with noise) and the page table that maps them back."""
+    S, C, Hkv, D = kc.shape
+    mp = (C + P - 1) // P
+    num_pages = S * mp + spare
+    g = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(num_pages, generator=g)[: S * mp].reshape(S, mp).to(torch.int32)
+    kp = _rand((num_pages, P, Hkv, D), 1.0, seed + 1)
+    vp = _rand((num_pages, P, Hkv, D), 1.0, seed + 2)
+    pad = mp * P - C
+    kpad = torch.cat([kc, kc[:, :pad]], dim=1) if pad else kc
+    vpad = torch.cat([vc, vc[:, :pad]], dim=1) if pad else vc
+    pt = perm.to(DEV)
+    kp[pt.reshape(-1).long()] = kpad.reshape(S * mp, P, Hkv, D)
+    vp[pt.reshape(-1).long()] = vpad.reshape(S * mp, P, Hkv, D)
+    return kp, vp, pt
+
+
+@pytest.mark.parametrize("P,mode,window", [(16, WITHIN, None), (16, MIX, None), (64, MIX, 300),
+                                           (1, MIX, None), (128, WITHIN, None), (4, MIX, 7)])
+def test_decode_paged_equals_contiguous(P, mode, window):
+    """Paged decode over shuffled pages gives the contiguous decode bit for
+    bit, and the append lands in the right page slots (checked against the
+    oracle's scatter)."""
+    cfg = si.DECODE
+    S, T = 5, 300
+    tb = [300, 0, 1, 129, 255]
+    qn, kn, vn, kc, vc, tbt = si.decode_inputs(cfg, device=DEV, S=S, T=T, tokens_before=tb)
+    kp, vp, pt = _paged_from(kc, vc, P, 7000 + P + mode)
+    kp0 = kp.clone()
+    ref = hd.decode_step(qn, kn, vn, kc, vc, tbt, cfg.n, T, mode, cfg.scale, window=window)
+    got = hd.decode_step_paged(qn, kn, vn, kp, vp, pt, tbt, cfg.n, T, mode, cfg.scale, window=window)
+    torch.cuda.synchronize()
+    assert torch.equal(ref.view(torch.int16), got.view(torch.int16))
+    want = si.bits(kp0)
+    pth = pt.cpu().numpy()
+    for q in range(S):
+        for s_ in range(cfg.n):
+            want = oracle.scatter_pages_ref(want, pth, q, tb[q] * cfg.n + s_, si.bits(kn[q, s_]))
+    assert np.array_equal(si.bits(kp), want)
+
+
+def test_decode_paged_oracle_on_gathered_pages():
+    """Paged decode against the oracle on the rows gathered back through the
+    page table (page size 32, mixing with a window)."""
+    cfg = si.DecodeCfg("dpg", 14, S=3, n=4, T=120, Hq=16, Hkv=4, D=128, scale=128 ** -0.5)
+    qn, kn, vn, kc, vc, tbt = si.decode_inputs(cfg, device=DEV, S=3, T=120, tokens_before=[120, 9, 64])
+    kp, vp, pt = _paged_from(kc, vc, 32, 7100)
+    out = hd.decode_step_paged(qn, kn, vn, kp, vp, pt, tbt, cfg.n, 120, MIX, cfg.scale, window=200)
+    torch.cuda.synchronize()
+    C = kc.shape[1]
+    k2 = oracle.gather_pages_ref(si.bits(kp), pt.cpu().numpy(), C)
+    v2 = oracle.gather_pages_ref(si.bits(vp), pt.cpu().numpy(), C)
+    ref = oracle.decode_ref(si.bits(qn), k2, v2, tbt.cpu().numpy(), cfg.n, MIX, cfg.scale, window=200)
+    assert_close(f64(out), ref, "paged decode vs oracle")
+
+
 def test_decode_idempotent_append_and_modes_share_cache():
     cfg = si.DECODE
     S, T = 4, 64
