@@ -236,6 +236,51 @@ def bench_decode(args, torch, hd, si):
     return res
 
 
+def bench_decode_stack(args, torch, hd, si):
+    """One decode step of every attention layer of the pages' 80B and 617B
+    schedules (paged caches, 32 sequences x 2048 tokens x 4 streams)."""
+    from sequence_length_latent_amd import schedule as sch
+    S, n, Hq, Hkv, D, P, T, W = 32, 4, 32, 8, 128, 64, 2048, DECODE_WINDOW
+    dev = torch.device("cuda")
+    mp = -(-((T + 1) * n) // P)
+    res = {}
+    for name in ("80B", "617B"):
+        kinds = sch.layer_kinds(name)
+        st = sch.PagedDecodeStack(kinds, S, n, Hq, Hkv, D, P, mp, W, device=dev)
+        for pool in st.k_pools + st.v_pools:
+            pool.normal_()
+        qs = [torch.randn((S, n, Hq, D), device=dev).to(torch.bfloat16) for _ in kinds]
+        ks = [torch.randn((S, n, Hkv, D), device=dev).to(torch.bfloat16) for _ in kinds]
+        vs = [torch.randn((S, n, Hkv, D), device=dev).to(torch.bfloat16) for _ in kinds]
+        outs = [torch.empty_like(q) for q in qs]
+        tb = torch.full((S,), T, dtype=torch.int32, device=dev)
+        ws = st.workspace(T)
+        st.step(qs, ks, vs, tb, T, D ** -0.5, outs, ws)
+        torch.cuda.synchronize()
+        reps = 3
+        e0, e1 = _events(2)
+        e0.record()
+        for _ in range(reps):
+            st.step(qs, ks, vs, tb, T, D ** -0.5, outs, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        entry = Hkv * D * 2 * 2
+        nbytes = sum(S * ((W + n - 1) if k == sch.SLIDING else (T + 1) * n) * entry for k in kinds)
+        res[name] = {"layers": len(kinds), "counts": sch.SCHEDULES[name], "ms_per_step": round(ms, 3),
+                     "bytes_per_step": nbytes, "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "unit": "GB/s", "peak": PEAK_HBM_GBS,
+                     "frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "tokens_per_s": round(S / (ms * 1e-3), 1)}
+        del st, qs, ks, vs, outs, ws
+        torch.cuda.empty_cache()
+    res["workload"] = (f"{S} sequences x {T} tokens x {n} streams cached, {Hq}/{Hkv} heads, head_dim {D}, "
+                       f"pages of {P} entries, sliding window {W} positions; one decode step of every "
+                       "attention layer (append + attention + combine per layer); tokens_per_s counts one "
+                       "token per sequence per step, attention only")
+    return res
+
+
 def bench_stack(args, torch, hd, si):
     """n=8, L=2048 stack of 3 within + 1 mixing layers vs the n=1 stack
     (4 causal layers at L=2048, same heads)."""
@@ -375,6 +420,9 @@ def main():
     if dec:
         print(f"[bench] decode done: within {dec['within']:.4f} ms mix {dec['mix']:.4f} ms",
               file=sys.stderr, flush=True)
+    dstack = None if args.no_decode else bench_decode_stack(args, torch, hd, si)
+    if dstack:
+        print("[bench] decode stack done", file=sys.stderr, flush=True)
     stack = None if args.no_stack else bench_stack(args, torch, hd, si)
     if stack:
         print("[bench] stack done", file=sys.stderr, flush=True)
@@ -476,6 +524,8 @@ def main():
         line["decode"]["traffic"] = measured_traffic("decode_attend_kernel", "decode.hip")
     if stack:
         line["stack"] = stack
+    if dstack:
+        line["decode_stack"] = dstack
     line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 

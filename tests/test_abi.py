@@ -181,6 +181,20 @@ def test_decode_paged_validation(lib):
     assert call(S=0, q=None, pt=None) == OK
 
 
+def test_layer_schedules():
+    """The pages' counts (80B: 6 full + 23 sliding-window + 20 within-stream of
+    49; 617B: 25 full + 69 within-stream of 94), each kind spread evenly."""
+    from sequence_length_latent_amd import schedule as sch
+    for name, total in (("80B", 49), ("617B", 94)):
+        kinds = sch.layer_kinds(name)
+        assert len(kinds) == total
+        for kind, count in sch.SCHEDULES[name].items():
+            at = [i for i, k in enumerate(kinds) if k == kind]
+            assert len(at) == count
+            gaps = [b - a for a, b in zip(at, at[1:])]
+            assert max(gaps, default=0) <= -(-total // count) + 1, (name, kind, gaps)
+
+
 def test_binding_rejects_host_tensors():
     import torch
     q = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)

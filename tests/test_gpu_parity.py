@@ -671,6 +671,40 @@ def test_decode_paged_oracle_on_gathered_pages():
     assert_close(f64(out), ref, "paged decode vs oracle")
 
 
+def test_decode_stack_three_layer_kinds():
+    """A paged multi-layer decode step (within-stream, sliding-window and full
+    mixing layers sharing one page table), each layer against the oracle."""
+    from sequence_length_latent_amd import schedule as sch
+    S, n, Hq, Hkv, D, P, T, W = 3, 4, 16, 4, 128, 16, 90, 150
+    kinds = [sch.WITHIN_STREAM, sch.SLIDING, sch.FULL]
+    mp = -(-((T + 1) * n) // P)
+    g = torch.Generator().manual_seed(7200)
+    pt = torch.randperm(S * mp + 5, generator=g)[: S * mp].reshape(S, mp).to(torch.int32).to(DEV)
+    st = sch.PagedDecodeStack(kinds, S, n, Hq, Hkv, D, P, mp, W, device=DEV, page_table=pt,
+                              num_pages=S * mp + 5)
+    for i in range(len(kinds)):
+        st.k_pools[i].copy_(_rand(st.k_pools[i].shape, 1.0, 7210 + i))
+        st.v_pools[i].copy_(_rand(st.v_pools[i].shape, 1.0, 7220 + i))
+    kp0 = [si.bits(x) for x in st.k_pools]
+    vp0 = [si.bits(x) for x in st.v_pools]
+    tb = torch.tensor([90, 3, 47], dtype=torch.int32, device=DEV)
+    qs = [_rand((S, n, Hq, D), 1.0, 7230 + i) for i in range(3)]
+    ks = [_rand((S, n, Hkv, D), 1.0, 7240 + i) for i in range(3)]
+    vs = [_rand((S, n, Hkv, D), 1.0, 7250 + i) for i in range(3)]
+    outs = [torch.empty_like(q) for q in qs]
+    st.step(qs, ks, vs, tb, T, D ** -0.5, outs, st.workspace(T))
+    torch.cuda.synchronize()
+    pth, tbh = pt.cpu().numpy(), tb.cpu().numpy()
+    C = mp * P
+    for i, kind in enumerate(kinds):
+        kc = oracle.gather_pages_ref(kp0[i], pth, C)
+        vc = oracle.gather_pages_ref(vp0[i], pth, C)
+        k2, v2 = oracle.decode_append_ref(kc, vc, si.bits(ks[i]), si.bits(vs[i]), tbh, n)
+        mode, window = st.layer_call(i)
+        ref = oracle.decode_ref(si.bits(qs[i]), k2, v2, tbh, n, mode, D ** -0.5, window=window)
+        assert_close(f64(outs[i]), ref, f"stack layer {i} ({kind})")
+
+
 def test_decode_idempotent_append_and_modes_share_cache():
     cfg = si.DECODE
     S, T = 4, 64
