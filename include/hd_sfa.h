@@ -282,7 +282,9 @@ hd_status sfa_decode_step(const uint16_t* q_new, const uint16_t* k_new,
  *   page_table        int32 [S, max_pages_per_seq], device memory; ids outside
  *                     [0, num_pages) are clamped into it on the device (no
  *                     access leaves the pool)
- *   page_size         a power of two (HD_ERR_SHAPE otherwise)
+ *   page_size         a power of two (HD_ERR_SHAPE otherwise); the pool may
+ *                     hold at most 2^32 rows (num_pages*page_size,
+ *                     HD_ERR_UNSUPPORTED beyond)
  *   max_tokens        as sfa_decode_step; (max_tokens+1)*n must fit in
  *                     max_pages_per_seq*page_size entries (HD_ERR_CAPACITY)
  *   mode              0 within-stream, 1 mixing

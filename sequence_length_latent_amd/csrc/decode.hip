@@ -132,6 +132,8 @@ decode_attend_kernel(const DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char smem_raw[SMEM_BYTES];
     __shared__ float sm_m[DNW][NQB * 32];
     __shared__ float sm_l[DNW][NQB * 32];
+    // PAGED: pool row of each key of the next two tiles (slot = tile parity)
+    __shared__ uint32_t row_tab[PAGED ? 2 * DT : 1];
     uint16_t* ks = reinterpret_cast<uint16_t*>(smem_raw);
     uint16_t* vt = ks + KS_ELEMS;
 
@@ -198,21 +200,43 @@ decode_attend_kernel(const DecodeArgs a) {
     // that two tiles (2 x 64 KB per workgroup) are in flight while a third is
     // consumed from LDS.  Rows past the split end are clamped to its last
     // row: the mask below gives them probability 0.
+    // PAGED: the pool rows of a tile's keys come from row_tab, filled two
+    // tiles ahead: the load of tile t also fetches (threads < DT, one key
+    // each) the page id of tile t+2 into pg, and the LDS store of tile t
+    // turns it into a pool row.  The data loads thus never wait on a table
+    // lookup (loads return in issue order, so a lookup issued just before
+    // them would also drain the tile already in flight).
     struct TileRegs {
         u32x4 k[K_CHUNKS];
         u32x4 v[V_PER][4];
+        int32_t pg;       // PAGED: raw page id of this thread's key of tile t+2
+        uint32_t pg_lo;   //        and that key's slot within its page
     };
     const uint32_t last_key = key_end - 1;
-    auto load_tile = [&](int t, TileRegs& r) {
+    const uint32_t pmask = (1u << a.pshift) - 1u;
+    // page id (raw) and slot of key j of tile t; keys past the split are clamped
+    auto fetch_page = [&](int t, int j, int32_t& pg, uint32_t& lo) {
+        const uint32_t key = min(key0 + (uint32_t)t * DT + (uint32_t)j, last_key);
+        const uint32_t e = key * rstride + view;
+        const uint32_t slot = min(e >> a.pshift, a.mpps - 1u);
+        pg = a.page_table[(uint64_t)seq * a.mpps + slot];
+        lo = e & pmask;
+    };
+    auto pool_row = [&](int32_t pg, uint32_t lo) -> uint32_t {
+        pg = pg < 0 ? 0 : (pg >= (int32_t)a.num_pages ? (int32_t)a.num_pages - 1 : pg);
+        return ((uint32_t)pg << a.pshift) | lo;
+    };
+    auto load_tile = [&](int t, TileRegs& r, int slot) {
         const uint32_t k0 = key0 + (uint32_t)t * DT;
+        [[maybe_unused]] const uint32_t* tab = row_tab + slot * DT;
 #pragma unroll
         for (int i = 0; i < K_CHUNKS; ++i) {
             const int cidx = tid + i * DTHREADS;
-            const uint32_t key = min(k0 + cidx / CPR, last_key);
             if constexpr (PAGED) {
-                const uint64_t row = paged_row(a.page_table, seq, key * rstride + view, a.pshift, a.mpps, a.num_pages);
+                const uint64_t row = tab[cidx / CPR];
                 r.k[i] = *reinterpret_cast<const u32x4*>(a.kc + row * erow + (uint64_t)kvh * D + (cidx % CPR) * 8);
             } else {
+                const uint32_t key = min(k0 + cidx / CPR, last_key);
                 r.k[i] = *reinterpret_cast<const u32x4*>(kbase + key * kstep + (cidx % CPR) * 8);
             }
         }
@@ -223,18 +247,23 @@ decode_attend_kernel(const DecodeArgs a) {
             const int dq = task / (DT / 4);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const uint32_t key = min(k0 + 4 * kq + q, last_key);
                 if constexpr (PAGED) {
-                    const uint64_t row = paged_row(a.page_table, seq, key * rstride + view, a.pshift, a.mpps,
-                                                   a.num_pages);
+                    const uint64_t row = tab[4 * kq + q];
                     r.v[i][q] = *reinterpret_cast<const u32x4*>(a.vc + row * erow + (uint64_t)kvh * D + dq * 8);
                 } else {
+                    const uint32_t key = min(k0 + 4 * kq + q, last_key);
                     r.v[i][q] = *reinterpret_cast<const u32x4*>(vbase + key * kstep + dq * 8);
                 }
             }
         }
+        if constexpr (PAGED) {
+            if (tid < DT) fetch_page(t + 2, tid, r.pg, r.pg_lo);
+        }
     };
-    auto store_tile = [&](const TileRegs& r) {
+    auto store_tile = [&](const TileRegs& r, int slot) {
+        if constexpr (PAGED) {
+            if (tid < DT) row_tab[slot * DT + tid] = pool_row(r.pg, r.pg_lo);
+        }
 #pragma unroll
         for (int i = 0; i < K_CHUNKS; ++i) {
             const int cidx = tid + i * DTHREADS;
@@ -329,19 +358,35 @@ decode_attend_kernel(const DecodeArgs a) {
         }
     };
 
-    TileRegs ra, rb;
-    load_tile(0, ra);
-    if (n_tiles > 1) load_tile(1, rb);
-    for (int t = 0; t < n_tiles; t += 2) {
-        store_tile(ra);
+    // tile t lives in ra (t even) or rb (t odd) and row_tab slot t & 1; the
+    // store of tile t fills that slot with tile t+2's rows once every load of
+    // tile t has read it (a barrier lies between them: the one after the
+    // previous compute, or for tile 0 the one after the first two loads)
+    if constexpr (PAGED) {
+        if (tid < DT) {
+            int32_t pg0, pg1;
+            uint32_t lo0, lo1;
+            fetch_page(0, tid, pg0, lo0);
+            fetch_page(1, tid, pg1, lo1);
+            row_tab[tid] = pool_row(pg0, lo0);
+            row_tab[DT + tid] = pool_row(pg1, lo1);
+        }
         __syncthreads();
-        if (t + 2 < n_tiles) load_tile(t + 2, ra);
+    }
+    TileRegs ra, rb;
+    load_tile(0, ra, 0);
+    if (n_tiles > 1) load_tile(1, rb, 1);
+    if constexpr (PAGED) __syncthreads();
+    for (int t = 0; t < n_tiles; t += 2) {
+        store_tile(ra, 0);
+        __syncthreads();
+        if (t + 2 < n_tiles) load_tile(t + 2, ra, 0);
         compute(t);
         __syncthreads();
         if (t + 1 < n_tiles) {
-            store_tile(rb);
+            store_tile(rb, 1);
             __syncthreads();
-            if (t + 3 < n_tiles) load_tile(t + 3, rb);
+            if (t + 3 < n_tiles) load_tile(t + 3, rb, 1);
             compute(t + 1);
             __syncthreads();
         }
@@ -612,9 +657,10 @@ extern "C" hd_status sfa_decode_step_paged(const uint16_t* q_new, const uint16_t
     using namespace hdsfa;
     if (page_size < 1 || (page_size & (page_size - 1)) != 0) return HD_ERR_SHAPE;
     if (num_pages < 1 || num_pages > 0x7fffffffLL || max_pages_per_seq < 1) return HD_ERR_SHAPE;
+    // pool row indices are 32-bit on the device
+    if ((uint64_t)num_pages * (uint64_t)page_size > 0x100000000ULL) return HD_ERR_UNSUPPORTED;
     if (window < 0 || (window > 0 && mode != 1) || window > 0x7fffffffLL) return HD_ERR_SHAPE;
     if (S > 0 && page_table == nullptr) return HD_ERR_NULL;
-    // row indices within the pool fit 32 bits + the page shift in 64-bit math
     Paging pg;
     pg.page_table = page_table;
     pg.pshift = (uint32_t)__builtin_ctz((unsigned)page_size);

@@ -179,6 +179,7 @@ def test_decode_paged_validation(lib):
     assert call(pt=None) == NULL
     assert call(wsb=16) == WS
     assert call(S=0, q=None, pt=None) == OK
+    assert call(P=1 << 16, num_pages=(1 << 16) + 1) == UNSUP   # pool rows past 32 bits
 
 
 def test_layer_schedules():
