@@ -38,7 +38,7 @@ constexpr int DT = 128;            // keys per workgroup tile (32 per wave)
 constexpr int DNW = 4;             // waves
 constexpr int DTHREADS = DNW * kWave;
 constexpr int DVP = DT + 8;        // transposed-V pitch (elements)
-constexpr int kTargetBlocks = 2048;
+constexpr int kTargetBlocks = 512;    // split-plan target: two resident workgroups on each of 256 CUs
 
 struct DecodeArgs {
     const uint16_t* q;         // [S, n, Hq, D]
@@ -113,8 +113,12 @@ decode_append_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ 
 // ---------------------------------------------------------------------------
 // 2. split-K attention
 // ---------------------------------------------------------------------------
+// One register set of tiles in flight.  With NQB = 1 two workgroups fit on a
+// compute unit, and each covers the other's load waits, start and merge (a
+// second register set would need the whole register file: one workgroup per
+// unit, measured slower; with NQB = 2 it spilled).
 template <int D, int NQB, bool PAGED>
-__global__ void __launch_bounds__(DTHREADS) __attribute__((amdgpu_waves_per_eu(1, 2)))
+__global__ void __launch_bounds__(DTHREADS) __attribute__((amdgpu_waves_per_eu(NQB == 1 ? 2 : 1, 2)))
 decode_attend_kernel(const DecodeArgs a) {
     constexpr int KP = D + 8;
     constexpr int KS_ELEMS = DT * KP;
@@ -196,10 +200,10 @@ decode_attend_kernel(const DecodeArgs a) {
         for (int i = 0; i < DBLK; ++i) oacc[qb][i] = f32x16{};
     }
 
-    // Tiles go global -> registers -> LDS.  Two register sets alternate so
-    // that two tiles (2 x 64 KB per workgroup) are in flight while a third is
-    // consumed from LDS.  Rows past the split end are clamped to its last
-    // row: the mask below gives them probability 0.
+    // Tiles go global -> registers -> LDS: the next tile (64 KB per
+    // workgroup) is in flight while the current one is consumed from LDS.
+    // Rows past the split end are clamped to its last row: the mask below
+    // gives them probability 0.
     // PAGED: the pool rows of a tile's keys come from row_tab, filled two
     // tiles ahead: the load of tile t also fetches (threads < DT, one key
     // each) the page id of tile t+2 into pg, and the LDS store of tile t
@@ -358,10 +362,10 @@ decode_attend_kernel(const DecodeArgs a) {
         }
     };
 
-    // tile t lives in ra (t even) or rb (t odd) and row_tab slot t & 1; the
-    // store of tile t fills that slot with tile t+2's rows once every load of
-    // tile t has read it (a barrier lies between them: the one after the
-    // previous compute, or for tile 0 the one after the first two loads)
+    // tile t reads row_tab slot t & 1; the store of tile t fills that slot
+    // with tile t+2's rows once every load of tile t has read it (a barrier
+    // lies between them: the one after the previous compute, or for tile 0
+    // the one after its load)
     if constexpr (PAGED) {
         if (tid < DT) {
             int32_t pg0, pg1;
@@ -373,23 +377,15 @@ decode_attend_kernel(const DecodeArgs a) {
         }
         __syncthreads();
     }
-    TileRegs ra, rb;
-    load_tile(0, ra, 0);
-    if (n_tiles > 1) load_tile(1, rb, 1);
+    TileRegs r;
+    load_tile(0, r, 0);
     if constexpr (PAGED) __syncthreads();
-    for (int t = 0; t < n_tiles; t += 2) {
-        store_tile(ra, 0);
+    for (int t = 0; t < n_tiles; ++t) {
+        store_tile(r, t & 1);
         __syncthreads();
-        if (t + 2 < n_tiles) load_tile(t + 2, ra, 0);
+        if (t + 1 < n_tiles) load_tile(t + 1, r, (t + 1) & 1);
         compute(t);
         __syncthreads();
-        if (t + 1 < n_tiles) {
-            store_tile(rb, 1);
-            __syncthreads();
-            if (t + 3 < n_tiles) load_tile(t + 3, rb, 1);
-            compute(t + 1);
-            __syncthreads();
-        }
     }
 
     // ---- merge the 4 waves' partial softmax states through LDS ----
