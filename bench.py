@@ -165,20 +165,21 @@ def bench_prefill(args, torch, hd, si):
     # training: forward with log-sum-exp, then the gradients, for both layers
     do = si.randn_bf16(q.shape, 1.0, 0x5FA0F00D, dev)
     bwd = {}
-    for name, mode in (("within", hd.WITHIN), ("mix", hd.MIX)):
-        o_, lse = hd.attn_fwd(q, k, v, cfg.n, cfg.scale, mode)
-        grads = hd.attn_bwd(q, k, v, do, lse, cfg.n, cfg.scale, mode)
+    for name, mode, win in (("within", hd.WITHIN, None), ("mix", hd.MIX, None),
+                            ("mix_window", hd.MIX, WINDOW)):
+        o_, lse = hd.attn_fwd(q, k, v, cfg.n, cfg.scale, mode, window=win)
+        grads = hd.attn_bwd(q, k, v, do, lse, cfg.n, cfg.scale, mode, window=win)
         torch.cuda.synchronize()
         reps = max(2, args.steps // 4)
         ew[0].record()
         for _ in range(reps):
-            hd.attn_fwd(q, k, v, cfg.n, cfg.scale, mode, out=o_, lse=lse)
+            hd.attn_fwd(q, k, v, cfg.n, cfg.scale, mode, out=o_, lse=lse, window=win)
         ew[1].record()
         torch.cuda.synchronize()
         t_f = ew[0].elapsed_time(ew[1]) / reps
         ew[0].record()
         for _ in range(reps):
-            hd.attn_bwd(q, k, v, do, lse, cfg.n, cfg.scale, mode, *grads)
+            hd.attn_bwd(q, k, v, do, lse, cfg.n, cfg.scale, mode, *grads, window=win)
         ew[1].record()
         torch.cuda.synchronize()
         bwd[name] = (t_f, ew[0].elapsed_time(ew[1]) / reps)
@@ -463,9 +464,11 @@ def main():
             "achieved": round(2.5 * pf[fk] / (pf["bwd"][name][1] * 1e-3) / 1e12, 2),
             "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS,
             "fwd_with_lse_ms": round(pf["bwd"][name][0], 4),
-            "note": "gradients dq, dk, dv of the n4 layer; useful work counted as 2.5x the "
-                    "forward's (five products per visible pair); not part of the step"}
-           for name, fk in (("within", "fw"), ("mix", "fm"))},
+            "note": "gradients dq, dk, dv of the n4 layer" + (f" (sliding window {WINDOW})"
+                                                                if name == "mix_window" else "")
+                    + "; useful work counted as 2.5x the forward's (five products per visible "
+                      "pair); not part of the step"}
+           for name, fk in (("within", "fw"), ("mix", "fm"), ("mix_window", "fmw"))},
         "hd_cyclic_replicate": {"ms": round(pf["t_cr"], 4), "bound": "hbm",
                                 "achieved": round(pf["cr_bytes"] / (pf["t_cr"] * 1e-3) / 1e9, 1),
                                 "unit": "GB/s", "peak": PEAK_HBM_GBS,

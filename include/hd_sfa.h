@@ -230,6 +230,42 @@ hd_status sfa_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        hipStream_t stream);
 
 /*
+ * sfa_attn_fwd_window -- the training forward of a sliding-window mixing
+ * layer: the output of sfa_mix_attn_window plus each row's log-sum-exp over
+ * its window (review, section Method: 23 of the 80B model's 49 layers mix
+ * streams with a sliding window, and the model trains on the expanded
+ * sequence).
+ *
+ *   lse      fp32 [B, Hq, n*L] (natural log over i - window < j <= i),
+ *            4-byte aligned, or NULL (then the call is sfa_mix_attn_window)
+ *   window   >= 1 (HD_ERR_SHAPE otherwise); window >= n*L gives exactly
+ *            sfa_attn_fwd in mode 1
+ * Other arguments, layouts and errors as sfa_mix_attn_window.
+ */
+hd_status sfa_attn_fwd_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              uint16_t* out, float* lse, int64_t B, int32_t n, int64_t L,
+                              int32_t Hq, int32_t Hkv, int32_t D, float softmax_scale,
+                              int64_t window, hipStream_t stream);
+
+/*
+ * sfa_attn_bwd_window -- gradients of a sliding-window mixing layer: the
+ * formulas of sfa_attn_bwd with P the softmax over the window
+ * i - window < j <= i (rebuilt from the lse of sfa_attn_fwd_window with the
+ * same window).
+ *
+ *   window   >= 1 (HD_ERR_SHAPE otherwise); window >= n*L gives exactly
+ *            sfa_attn_bwd in mode 1
+ * Other arguments (no mode), the workspace size, layouts, precision and
+ * errors as sfa_attn_bwd.
+ */
+hd_status sfa_attn_bwd_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const uint16_t* dout, const float* lse,
+                              uint16_t* dq, uint16_t* dk, uint16_t* dv, int64_t B, int32_t n,
+                              int64_t L, int32_t Hq, int32_t Hkv, int32_t D, float softmax_scale,
+                              int64_t window, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/*
  * sfa_decode_workspace_size -- bytes of device workspace sfa_decode_step
  * needs for these sizes (fp32 split partials).  Returns 0 for invalid sizes.
  */

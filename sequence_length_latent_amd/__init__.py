@@ -114,10 +114,12 @@ def _attn(fn_name: str, q, k, v, n: int, scale: float, out, window=None, lse=Non
     if out.shape != q.shape:
         raise ValueError("out must match q")
     extra = () if window is None else (int(window),)
-    if mode is not None:
+    if lse is not None:
+        # training forward: mode (sfa_attn_fwd) or window (sfa_attn_fwd_window)
+        last = int(mode) if mode is not None else int(window)
         st = getattr(load(), fn_name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                       lse.data_ptr(), B, n, N // n, Hq, Hkv, D, float(scale),
-                                      int(mode), _stream())
+                                      last, _stream())
     else:
         st = getattr(load(), fn_name)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                       B, n, N // n, Hq, Hkv, D, float(scale), *extra, _stream())
@@ -141,9 +143,10 @@ def mix_attn_window(q, k, v, n: int, scale: float, window: int, out=None):
     return _attn("sfa_mix_attn_window", q, k, v, n, scale, out, window)
 
 
-def attn_fwd(q, k, v, n: int, scale: float, mode: int, out=None, lse=None):
+def attn_fwd(q, k, v, n: int, scale: float, mode: int, out=None, lse=None, window=None):
     """Forward of a prefill layer (mode WITHIN or MIX) with its log-sum-exp:
-    returns (out [B, n*L, Hq, D] bf16, lse [B, Hq, n*L] fp32, natural log)."""
+    returns (out [B, n*L, Hq, D] bf16, lse [B, Hq, n*L] fp32, natural log).
+    ``window`` (MIX only): the sliding-window layer (sfa_attn_fwd_window)."""
     _need(q, "q", torch.bfloat16, 4)
     B, N, Hq, _ = q.shape
     if lse is None:
@@ -151,14 +154,22 @@ def attn_fwd(q, k, v, n: int, scale: float, mode: int, out=None, lse=None):
     _need(lse, "lse", torch.float32, 3)
     if tuple(lse.shape) != (B, Hq, N):
         raise ValueError("lse must be [B, Hq, n*L]")
-    out = _attn("sfa_attn_fwd", q, k, v, n, scale, out, lse=lse, mode=mode)
+    if window is not None:
+        if mode != MIX:
+            raise ValueError("a window applies to mixing layers only")
+        out = _attn("sfa_attn_fwd_window", q, k, v, n, scale, out, window=window, lse=lse)
+    else:
+        out = _attn("sfa_attn_fwd", q, k, v, n, scale, out, lse=lse, mode=mode)
     return out, lse
 
 
 def attn_bwd(q, k, v, dout, lse, n: int, scale: float, mode: int, dq=None, dk=None,
-             dv=None, workspace=None):
+             dv=None, workspace=None, window=None):
     """Gradients of a prefill layer: returns (dq, dk, dv) in bf16.  ``lse`` is
-    the forward's (attn_fwd with the same arguments)."""
+    the forward's (attn_fwd with the same arguments).  ``window`` (MIX only):
+    the sliding-window layer (sfa_attn_bwd_window)."""
+    if window is not None and mode != MIX:
+        raise ValueError("a window applies to mixing layers only")
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
         _need(t, nm, torch.bfloat16, 4)
     _need(lse, "lse", torch.float32, 3)
@@ -183,11 +194,13 @@ def attn_bwd(q, k, v, dout, lse, n: int, scale: float, mode: int, dq=None, dk=No
     need = int(lib.sfa_attn_bwd_workspace_size(B, n, N // n, Hq))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    st = lib.sfa_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+    fn = "sfa_attn_bwd" if window is None else "sfa_attn_bwd_window"
+    last = int(mode) if window is None else int(window)
+    st = getattr(lib, fn)(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
                           lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, n, N // n,
-                          Hq, Hkv, D, float(scale), int(mode), workspace.data_ptr(),
+                          Hq, Hkv, D, float(scale), last, workspace.data_ptr(),
                           workspace.numel() * workspace.element_size(), _stream())
-    check("sfa_attn_bwd", st)
+    check(fn, st)
     return dq, dk, dv
 
 

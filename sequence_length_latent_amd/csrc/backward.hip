@@ -25,6 +25,11 @@
 //                 dK^T += Q^T dS over every query head of the KV group and the
 //                 query tiles at or after the keys (one key per lane, Q / dO
 //                 tiles staged in LDS, dO^T and Q^T through transpose reads).
+// Sliding-window mixing layers (sfa_attn_bwd_window; the review's Method:
+// mixing layers follow the base model's pattern, sliding-window or full):
+// query i sees keys i - W < j <= i, so dq_kernel starts at the first key tile
+// inside a tile's windows and dkv_kernel stops at the last query tile whose
+// windows reach the keys (WIN instances; the masks drop i - j >= W).
 // All products are v_mfma_f32_32x32x16_bf16 (bf16 operands, fp32 accumulate).
 // The gradients sum many unnormalised terms (a key collects dS from every
 // later query of every head of its group), so P and dS enter the products as
@@ -66,6 +71,7 @@ struct BwdArgs {
     uint32_t n_ktiles, n_kitems;               // dkv work items
     float c;                 // scale * log2(e)
     float scale;
+    uint32_t window;         // sliding window W (WIN instances only; W < len)
 };
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -96,7 +102,7 @@ __device__ __forceinline__ bf16x8 lds_tr(const unsigned char* p0, const unsigned
 // ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool WIN>
 __global__ void __launch_bounds__(NWQ * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 dq_kernel(const BwdArgs a) {
     constexpr int ROWB = D * 2;
@@ -128,6 +134,13 @@ dq_kernel(const BwdArgs a) {
     const uint32_t wg_end = min(a.len, (qtile + 1) * BT);
     const int n_kt = (int)((wg_end + BN - 1) / BN);
     const int last = q0 < a.len ? (int)((min(a.len, q0 + MQ) + BN - 1) / BN) - 1 : -1;
+    // first key tile of the workgroup's windows and of this wave's (0 without a window)
+    int m_lo = 0, wave_lo = 0;
+    if constexpr (WIN) {
+        const uint32_t f0 = qtile * BT;
+        m_lo = (int)((f0 >= a.window ? f0 - a.window + 1 : 0u) / BN);
+        wave_lo = (int)((q0 >= a.window ? q0 - a.window + 1 : 0u) / BN);
+    }
     const uint32_t qi = q0 + l32;                       // this lane's query row
     const uint32_t qr = min(qi, a.len - 1u);
 
@@ -194,16 +207,16 @@ dq_kernel(const BwdArgs a) {
     auto pass = [&](auto second) {
         constexpr bool SECOND = decltype(second)::value;
         float dsum[4] = {0.f, 0.f, 0.f, 0.f};
-        issue(kview, 0, kbuf(0));
-        issue(vview, 0, vbuf(0));
-        for (int m = 0; m < n_kt; ++m) {
+        issue(kview, m_lo, kbuf(m_lo));
+        issue(vview, m_lo, vbuf(m_lo));
+        for (int m = m_lo; m < n_kt; ++m) {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             if (m + 1 < n_kt) {
                 issue(kview, m + 1, kbuf(m + 1));
                 issue(vview, m + 1, vbuf(m + 1));
             }
-            if (m > last) continue;
+            if (m > last || m < wave_lo) continue;
             const unsigned char* kt = kbuf(m);
             const unsigned char* vt = vbuf(m);
             // S^T = K Q^T and dP^T = V dO^T (64 keys x 32 queries)
@@ -215,7 +228,7 @@ dq_kernel(const BwdArgs a) {
                     st[kb] = mfma(lds16(kt + kb * 32 * ROWB + doff[e]), qf[e], st[kb]);
                     dpt[kb] = mfma(lds16(vt + kb * 32 * ROWB + doff[e]), dof[e], dpt[kb]);
                 }
-            // P^T = 2^(c s - lse2), masked past the query
+            // P^T = 2^(c s - lse2), masked past the query (and before its window)
             const int rel = (int)qi - m * BN - 4 * hh;
             const bool diag = m == last;
             bf16x8 dsf[4], dsl[4];
@@ -228,6 +241,7 @@ dq_kernel(const BwdArgs a) {
                     const int off = kb * 32 + 8 * (it >> 2) + (it & 3);
                     float p = fast_exp2(__builtin_fmaf(st[kb][it], a.c, -lse2));
                     if (diag && off > rel) p = 0.f;
+                    if (WIN && off <= rel - (int)a.window) p = 0.f;       // key before the window
                     if constexpr (SECOND) v8[j] = p * (dpt[kb][it] - dl);   // dS^T
                     else dsum[j & 3] = __builtin_fmaf(p, dpt[kb][it], dsum[j & 3]);
                 }
@@ -270,7 +284,7 @@ dq_kernel(const BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dK, dV
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool WIN>
 __global__ void __launch_bounds__(NWK * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
 dkv_kernel(const BwdArgs a) {
     constexpr int ROWB = D * 2;
@@ -310,9 +324,14 @@ dkv_kernel(const BwdArgs a) {
         vf[e] = *reinterpret_cast<const bf16x8*>(a.v + koff + (2 * e + hh) * 8);
     }
 
-    // stages: (query head of the group, query tile at or after the keys)
+    // stages: (query head of the group, query tile at or after the keys and,
+    // with a window, at or before the last query whose window reaches them)
     const uint32_t qt_lo = k0 / BN;
-    const uint32_t nq = (a.len + BN - 1) / BN;
+    uint32_t nq = (a.len + BN - 1) / BN;
+    if constexpr (WIN) {
+        const uint32_t k_last = min(a.len, k0 + KV_TILE) - 1u;
+        nq = min(nq, (k_last + a.window - 1u) / BN + 1u);
+    }
     const uint32_t per_head = nq - qt_lo;
     const uint32_t n_stage = a.G * per_head;
     const uint32_t q_row_b = (uint32_t)a.q_row * 2u;
@@ -385,6 +404,7 @@ dkv_kernel(const BwdArgs a) {
         for (int qb = 0; qb < BN / MQ; ++qb) {
             const uint32_t rs = r0 + qb * MQ;             // first query of the block
             if (rs + MQ - 1 < kw0 || rs >= a.len) continue;   // all queries before the keys
+            if (WIN && rs >= kw0 + MQ - 1 + a.window) continue;   // all past the keys' windows
             // S = Q K^T and dP = dO V^T (32 queries x 32 keys)
             f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -409,6 +429,7 @@ dkv_kernel(const BwdArgs a) {
                         const int off = 8 * g4 + j;
                         float p = fast_exp2(__builtin_fmaf(s[it], a.c, -l4[j] * kLog2e));
                         if (off + rel < 0 || rs + (uint32_t)off + 4u * hh >= a.len) p = 0.f;
+                        if (WIN && off + rel >= (int)a.window) p = 0.f;   // query past the window
                         pv[4 * g2 + j] = p;
                         dv8[4 * g2 + j] = p * (dp[it] - d4[j]);
                     }
@@ -452,7 +473,9 @@ dkv_kernel(const BwdArgs a) {
 hd_status launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                      const uint16_t* dout, const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
                      int64_t B, int32_t n, int64_t L, int32_t Hq, int32_t Hkv, int32_t D, float scale,
-                     int32_t mode, void* workspace, size_t ws_bytes, hipStream_t stream) {
+                     int32_t mode, void* workspace, size_t ws_bytes, hipStream_t stream,
+                     int64_t window = 0) {
+    // window: 0 = plain causal, else >= 1 (mixing only; checked by the caller)
     if (B < 0 || L < 0 || n < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return HD_ERR_SHAPE;
     if (mode != 0 && mode != 1) return HD_ERR_SHAPE;
     if (D != 64 && D != 128) return HD_ERR_UNSUPPORTED;
@@ -497,14 +520,28 @@ hd_status launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     a.n_kitems = (uint32_t)kitems;
     a.c = scale * kLog2e;
     a.scale = scale;
+    // a window at least as long as the view masks nothing: the causal kernels
+    const bool win = window > 0 && window < (int64_t)a.len;
+    a.window = win ? (uint32_t)window : 0u;
 
     // dq_kernel writes delta, which dkv_kernel reads (same stream, in order)
+    const dim3 gq(a.n_items), gk(a.n_kitems), bq(NWQ * kWave), bk(NWK * kWave);
     if (D == 128) {
-        dq_kernel<128><<<dim3(a.n_items), dim3(NWQ * kWave), 0, stream>>>(a);
-        dkv_kernel<128><<<dim3(a.n_kitems), dim3(NWK * kWave), 0, stream>>>(a);
+        if (win) {
+            dq_kernel<128, true><<<gq, bq, 0, stream>>>(a);
+            dkv_kernel<128, true><<<gk, bk, 0, stream>>>(a);
+        } else {
+            dq_kernel<128, false><<<gq, bq, 0, stream>>>(a);
+            dkv_kernel<128, false><<<gk, bk, 0, stream>>>(a);
+        }
     } else {
-        dq_kernel<64><<<dim3(a.n_items), dim3(NWQ * kWave), 0, stream>>>(a);
-        dkv_kernel<64><<<dim3(a.n_kitems), dim3(NWK * kWave), 0, stream>>>(a);
+        if (win) {
+            dq_kernel<64, true><<<gq, bq, 0, stream>>>(a);
+            dkv_kernel<64, true><<<gk, bk, 0, stream>>>(a);
+        } else {
+            dq_kernel<64, false><<<gq, bq, 0, stream>>>(a);
+            dkv_kernel<64, false><<<gk, bk, 0, stream>>>(a);
+        }
     }
     return launch_status();
 }
@@ -526,4 +563,15 @@ extern "C" hd_status sfa_attn_bwd(const uint16_t* q, const uint16_t* k, const ui
                                   size_t workspace_bytes, hipStream_t stream) {
     return hdsfa::launch_bwd(q, k, v, dout, lse, dq, dk, dv, B, n, L, Hq, Hkv, D, softmax_scale,
                              mode, workspace, workspace_bytes, stream);
+}
+
+extern "C" hd_status sfa_attn_bwd_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                         const uint16_t* dout, const float* lse,
+                                         uint16_t* dq, uint16_t* dk, uint16_t* dv, int64_t B,
+                                         int32_t n, int64_t L, int32_t Hq, int32_t Hkv, int32_t D,
+                                         float softmax_scale, int64_t window, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream) {
+    if (window < 1 || window > 0x7fffffffLL) return HD_ERR_SHAPE;
+    return hdsfa::launch_bwd(q, k, v, dout, lse, dq, dk, dv, B, n, L, Hq, Hkv, D, softmax_scale,
+                             /*mode=*/1, workspace, workspace_bytes, stream, window);
 }

@@ -714,3 +714,13 @@ extern "C" hd_status sfa_mix_attn_window(const uint16_t* q, const uint16_t* k,
                                  stream, /*within=*/false, window);
 }
 
+
+extern "C" hd_status sfa_attn_fwd_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                         uint16_t* out, float* lse, int64_t B, int32_t n, int64_t L,
+                                         int32_t Hq, int32_t Hkv, int32_t D, float softmax_scale,
+                                         int64_t window, hipStream_t stream) {
+    if (window < 1) return HD_ERR_SHAPE;
+    if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return HD_ERR_SHAPE;
+    return hdsfa::launch_prefill(q, k, v, out, B, n, L, Hq, Hkv, D, softmax_scale, stream,
+                                 /*within=*/false, window, lse);
+}

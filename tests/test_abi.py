@@ -33,6 +33,7 @@ def test_every_declared_symbol_is_exported(lib):
                           "hd_final_stream_rows", "hd_cyclic_replicate", "sfa_stream_attn",
                           "sfa_mix_attn", "sfa_mix_attn_window", "sfa_attn_fwd",
                           "sfa_attn_bwd_workspace_size", "sfa_attn_bwd",
+                          "sfa_attn_fwd_window", "sfa_attn_bwd_window",
                           "sfa_decode_workspace_size", "sfa_decode_step",
                           "sfa_decode_step_window", "sfa_decode_step_paged"}
     for name in names:
@@ -108,6 +109,21 @@ def test_training_entry_validation(lib):
     assert b(*args, 1, 2, 8, 4, 2, 128, 1.0, 0, FAKE, 16, None) == WS                   # workspace
     assert b(None, *args[1:], 1, 2, 8, 4, 2, 128, 1.0, 0, FAKE, 1 << 20, None) == NULL
     assert b(*args, 0, 2, 8, 4, 2, 128, 1.0, 0, FAKE, 0, None) == OK                    # empty
+
+
+def test_training_window_validation(lib):
+    f, b = lib.sfa_attn_fwd_window, lib.sfa_attn_bwd_window
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 8, 4, 2, 128, 1.0, 0, None) == SHAPE     # window < 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE + 2, 1, 2, 8, 4, 2, 128, 1.0, 4, None) == SHAPE  # lse align
+    assert f(None, FAKE, FAKE, FAKE, FAKE, 1, 2, 8, 4, 2, 128, 1.0, 4, None) == NULL
+    assert f(None, None, None, None, None, 0, 2, 8, 4, 2, 128, 1.0, 4, None) == OK        # empty
+    args = [FAKE] * 8
+    assert b(*args, 1, 2, 8, 4, 2, 128, 1.0, 0, FAKE, 1 << 20, None) == SHAPE           # window < 1
+    assert b(*args, 1, 2, 8, 4, 2, 128, 1.0, 1 << 40, FAKE, 1 << 20, None) == SHAPE     # > 2^31 - 1
+    assert b(*args, 1, 2, 8, 4, 3, 128, 1.0, 4, FAKE, 1 << 20, None) == SHAPE           # Hq % Hkv
+    assert b(*args, 1, 2, 8, 4, 2, 96, 1.0, 4, FAKE, 1 << 20, None) == UNSUP            # D
+    assert b(*args, 1, 2, 8, 4, 2, 128, 1.0, 4, FAKE, 16, None) == WS                   # workspace
+    assert b(*args, 0, 2, 8, 4, 2, 128, 1.0, 4, FAKE, 0, None) == OK                    # empty
 
 
 def test_window_validation(lib):

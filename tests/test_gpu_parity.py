@@ -364,6 +364,95 @@ def test_attn_bwd_n4_full_size_one_group(mode):
     assert_close(f64(dv[:1, :, :1].cpu()), rv, f"n4 dv mode={mode}")
 
 
+WIN_BWD_SWEEP = [
+    # n, B, L, Hq, Hkv, D, W (positions of the interleaved order)
+    (2, 1, 70, 4, 2, 128, 7),        # inside a 64-row tile
+    (3, 1, 45, 8, 2, 64, 64),        # one tile
+    (4, 1, 129, 8, 1, 128, 65),      # a tile and one; partial last 128-key tile
+    (4, 1, 129, 8, 1, 128, 300),     # across 128-key tiles
+    (2, 2, 100, 16, 2, 128, 199),    # W = N - 1, P = 8 packing
+    (1, 1, 300, 2, 2, 128, 129),     # P = 1
+]
+
+
+@pytest.mark.parametrize("n,B,L,Hq,Hkv,D,W", WIN_BWD_SWEEP)
+def test_attn_window_training_sweep(n, B, L, Hq, Hkv, D, W):
+    """Sliding-window mixing layer: the training forward equals the plain
+    windowed forward bit for bit, its lse and the gradients match the oracle."""
+    seed = 7300 + 31 * n + 7 * L + Hq + D + W
+    N = n * L
+    scale = D ** -0.5
+    q = _rand((B, N, Hq, D), 1.0, seed)
+    k = _rand((B, N, Hkv, D), 1.0, seed + 1)
+    v = _rand((B, N, Hkv, D), 1.0, seed + 2)
+    do = _rand((B, N, Hq, D), 1.0, seed + 3)
+    out, lse = hd.attn_fwd(q, k, v, n, scale, MIX, window=W)
+    plain = hd.mix_attn_window(q, k, v, n, scale, W)
+    assert torch.equal(out.view(torch.int16), plain.view(torch.int16))
+    dq, dk, dv = hd.attn_bwd(q, k, v, do, lse, n, scale, MIX, window=W)
+    rq, rk, rv, rl = oracle.prefill_backward_ref(si.bits(q.cpu()), si.bits(k.cpu()), si.bits(v.cpu()),
+                                                 si.bits(do.cpu()), n, MIX, scale, window=W)
+    what = f"window bwd n={n} L={L} H={Hq}/{Hkv} D={D} W={W}"
+    _assert_lse(lse.permute(0, 2, 1).cpu().numpy().astype(np.float64), rl, "lse " + what)
+    assert_close(f64(dq.cpu()), rq, "dq " + what)
+    assert_close(f64(dk.cpu()), rk, "dk " + what)
+    assert_close(f64(dv.cpu()), rv, "dv " + what)
+
+
+def test_attn_window_one_training():
+    """W = 1: every query sees only its own key, so P = 1, dV_j = the sum of
+    dO_j over the KV group's query heads, and dQ = dK = 0 (up to the rounding
+    of lse)."""
+    n, L, Hq, Hkv, D = 2, 40, 4, 2, 64
+    N = n * L
+    q = _rand((1, N, Hq, D), 1.0, 7400)
+    k = _rand((1, N, Hkv, D), 1.0, 7401)
+    v = _rand((1, N, Hkv, D), 1.0, 7402)
+    do = _rand((1, N, Hq, D), 1.0, 7403)
+    out, lse = hd.attn_fwd(q, k, v, n, 0.125, MIX, window=1)
+    dq, dk, dv = hd.attn_bwd(q, k, v, do, lse, n, 0.125, MIX, window=1)
+    want = do.float().reshape(1, N, Hkv, Hq // Hkv, D).sum(3)
+    assert torch.all((dv.float() - want).abs() <= want.abs() * 2.0 ** -7 + 1e-5)
+    assert float(dq.float().abs().max()) < 1e-4 and float(dk.float().abs().max()) < 1e-4
+
+
+def test_attn_window_training_long_window_is_full():
+    """W >= N: the windowed training forward and gradients are bitwise those
+    of the full mixing layer."""
+    n, B, L, Hq, Hkv, D = 3, 1, 50, 8, 2, 128
+    N = n * L
+    q = _rand((B, N, Hq, D), 1.0, 7450)
+    k = _rand((B, N, Hkv, D), 1.0, 7451)
+    v = _rand((B, N, Hkv, D), 1.0, 7452)
+    do = _rand((B, N, Hq, D), 1.0, 7453)
+    out, lse = hd.attn_fwd(q, k, v, n, D ** -0.5, MIX)
+    outw, lsew = hd.attn_fwd(q, k, v, n, D ** -0.5, MIX, window=N)
+    assert torch.equal(out.view(torch.int16), outw.view(torch.int16)) and torch.equal(lse, lsew)
+    a = hd.attn_bwd(q, k, v, do, lse, n, D ** -0.5, MIX)
+    b = hd.attn_bwd(q, k, v, do, lse, n, D ** -0.5, MIX, window=N + 5)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def test_attn_window_training_n4_full_size_one_group():
+    """The n4 workload at W = 1024 (256 tokens at n = 4), full size; the oracle
+    computes batch 0, KV head 0 (its four query heads) over every row."""
+    cfg = si.N4
+    W = 1024
+    q, k, v = si.prefill_qkv(cfg, device=DEV)
+    do = _rand(q.shape, 1.0, 7500)
+    out, lse = hd.attn_fwd(q, k, v, cfg.n, cfg.scale, MIX, window=W)
+    dq, dk, dv = hd.attn_bwd(q, k, v, do, lse, cfg.n, cfg.scale, MIX, window=W)
+    torch.cuda.synchronize()
+    G = cfg.Hq // cfg.Hkv
+    rq, rk, rv, _ = oracle.prefill_backward_ref(si.bits(q[:1].cpu()), si.bits(k[:1].cpu()),
+                                                si.bits(v[:1].cpu()), si.bits(do[:1].cpu()),
+                                                cfg.n, MIX, cfg.scale, window=W, heads=[0])
+    assert_close(f64(dq[:1, :, :G].cpu()), rq, "n4 window dq")
+    assert_close(f64(dk[:1, :, :1].cpu()), rk, "n4 window dk")
+    assert_close(f64(dv[:1, :, :1].cpu()), rv, "n4 window dv")
+
+
 def test_attn_bwd_deterministic():
     n, B, L, Hq, Hkv, D = 3, 1, 90, 8, 2, 128
     N = n * L
