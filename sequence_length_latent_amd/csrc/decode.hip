@@ -19,7 +19,9 @@
 //                  (V transposed for the V^T operand) and both contractions
 //                  run on v_mfma_f32_32x32x16_bf16; 4 waves take 32 keys each
 //                  of a 128-key tile and merge their (max, sum, O) at the end;
-//   3. combine  -- merges the per-split partials (fp32) into bf16 output.
+//   3. combine  -- merges the per-split partials (fp32) into bf16 output
+//                  (skipped when every view is one split: the attention
+//                  kernel then writes the normalised bf16 rows itself).
 // Sliding-window mixing (sfa_decode_step_window; the review's Method: mixing
 // layers follow the base model's pattern, sliding-window or full): query
 // (T, s) at p = T*n + s reads entries p - W < j <= p, so the view starts at
@@ -55,6 +57,8 @@ struct DecodeArgs {
     float c;
     const int32_t* page_table; // [S, mpps] (PAGED instances)
     uint32_t pshift, mpps, num_pages;
+    uint16_t* out;             // [S, n, Hq, D]: written here when direct
+    uint32_t direct;           // one split per view: the merged row is the output
 };
 
 // pool row of entry e of sequence seq (page ids outside the pool are clamped
@@ -423,6 +427,15 @@ decode_attend_kernel(const DecodeArgs a) {
             l += f * sm_l[w][row];
         }
         const uint32_t r = r_base + row;
+        if (a.direct) {
+            // the combine of a single split: its weight is 2^0 = 1, so the
+            // output is o / l rounded to bf16
+            const uint32_t s = r / a.G;
+            const uint32_t gh = r - s * a.G;
+            const __bf16 hv = (__bf16)(o / l);
+            a.out[(((uint64_t)seq * a.n + s) * a.Hq + kvh * a.G + gh) * D + d] = __builtin_bit_cast(uint16_t, hv);
+            continue;
+        }
         float* part = a.ws + ((((uint64_t)seq * a.Hkv + kvh) * a.R + r) * a.nsplit + sp) * (D + 2);
         if (d == 0) {
             part[0] = M;
@@ -594,6 +607,8 @@ hd_status decode_step(const uint16_t* q_new, const uint16_t* k_new, const uint16
     a.pshift = pg.pshift;
     a.mpps = pg.mpps;
     a.num_pages = pg.num_pages;
+    a.out = out;
+    a.direct = plan.nsplit == 1 ? 1u : 0u;
     const uint32_t rows = within ? G : R;
     const dim3 grid(plan.nsplit, (uint32_t)Hkv * (within ? (uint32_t)n : 1u), (uint32_t)S);
     if (D == 128) {
@@ -609,8 +624,9 @@ hd_status decode_step(const uint16_t* q_new, const uint16_t* k_new, const uint16
     }
     hd_status st = launch_status();
     if (st != HD_OK) return st;
+    if (a.direct) return HD_OK;
 
-    // 3. combine
+    // 3. combine (more than one split per view)
     const uint64_t total = (uint64_t)S * Hkv * R * D;
     if (total > 0x7fffffffULL) return HD_ERR_UNSUPPORTED;
     const uint32_t blocks = (uint32_t)((total + 255) / 256);
