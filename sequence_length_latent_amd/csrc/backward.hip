@@ -405,50 +405,76 @@ dkv_kernel(const BwdArgs a) {
             const uint32_t rs = r0 + qb * MQ;             // first query of the block
             if (rs + MQ - 1 < kw0 || rs >= a.len) continue;   // all queries before the keys
             if (WIN && rs >= kw0 + MQ - 1 + a.window) continue;   // all past the keys' windows
-            // S = Q K^T and dP = dO V^T (32 queries x 32 keys)
+            // S = Q K^T and dP = dO V^T (32 queries x 32 keys); every fragment
+            // read is issued before the products that use it
+            bf16x8 qa[DSTEPS], oa[DSTEPS];
+#pragma unroll
+            for (int e = 0; e < DSTEPS; ++e) {
+                qa[e] = lds16(qt + qb * MQ * ROWB + doff[e]);
+                oa[e] = lds16(ot + qb * MQ * ROWB + doff[e]);
+            }
             f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
             for (int e = 0; e < DSTEPS; ++e) {
-                s = mfma(lds16(qt + qb * MQ * ROWB + doff[e]), kf[e], s);
-                dp = mfma(lds16(ot + qb * MQ * ROWB + doff[e]), vf[e], dp);
+                s = mfma(qa[e], kf[e], s);
+                dp = mfma(oa[e], vf[e], dp);
             }
-            // lane: key column; entries: query rows 8*(i/4) + 4hh + i%4 of the block
-            const int rel = (int)rs + 4 * hh - (int)key;   // query - key = rel + off
-            bf16x8 pf[2], pl[2], dsf[2], dsl[2];
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                f32x8 pv, dv8;
-#pragma unroll
-                for (int g2 = 0; g2 < 2; ++g2) {
-                    const int g4 = 2 * cc + g2;
-                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(lt + qb * MQ + 8 * g4 + 4 * hh);
-                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(dt + qb * MQ + 8 * g4 + 4 * hh);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int it = 4 * g4 + j;
-                        const int off = 8 * g4 + j;
-                        float p = fast_exp2(__builtin_fmaf(s[it], a.c, -l4[j] * kLog2e));
-                        if (off + rel < 0 || rs + (uint32_t)off + 4u * hh >= a.len) p = 0.f;
-                        if (WIN && off + rel >= (int)a.window) p = 0.f;   // query past the window
-                        pv[4 * g2 + j] = p;
-                        dv8[4 * g2 + j] = p * (dp[it] - d4[j]);
-                    }
-                }
-                split_bf16(pv, pf[cc], pl[cc]);
-                split_bf16(dv8, dsf[cc], dsl[cc]);
-            }
-            // dV^T += dO^T P,  dK^T += Q^T dS
+            // the transposed operands of dV^T and dK^T, read while P and dS form
+            bf16x8 ot8[DBLK][2], qt8[DBLK][2];
 #pragma unroll
             for (int db = 0; db < DBLK; ++db)
 #pragma unroll
                 for (int cc = 0; cc < 2; ++cc) {
                     const uint32_t ro = (uint32_t)(qb * MQ + cc * 16) * ROWB;
-                    const bf16x8 ot8 = lds_tr(ot + ro + toff[0][db], ot + ro + toff[1][db]);
-                    const bf16x8 qt8 = lds_tr(qt + ro + toff[0][db], qt + ro + toff[1][db]);
-                    dvt[db] = mfma(ot8, pf[cc], dvt[db]);
-                    dvt[db] = mfma(ot8, pl[cc], dvt[db]);
-                    dkt[db] = mfma(qt8, dsf[cc], dkt[db]);
-                    dkt[db] = mfma(qt8, dsl[cc], dkt[db]);
+                    ot8[db][cc] = lds_tr(ot + ro + toff[0][db], ot + ro + toff[1][db]);
+                    qt8[db][cc] = lds_tr(qt + ro + toff[0][db], qt + ro + toff[1][db]);
+                }
+            // lane: key column; entries: query rows 8*(i/4) + 4hh + i%4 of the block
+            const int rel = (int)rs + 4 * hh - (int)key;   // query - key = rel + off
+            bf16x8 pf[2], pl[2], dsf[2], dsl[2];
+            // masks only in blocks that meet the keys' diagonal, the view end or
+            // (WIN) the far edge of the keys' windows: a wave-uniform choice, and
+            // a select (no branch) per element where they apply
+            auto probs = [&](auto masked) __attribute__((always_inline)) {
+                constexpr bool MASKED = decltype(masked)::value;
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) {
+                    f32x8 pv, dv8;
+#pragma unroll
+                    for (int g2 = 0; g2 < 2; ++g2) {
+                        const int g4 = 2 * cc + g2;
+                        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lt + qb * MQ + 8 * g4 + 4 * hh);
+                        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dt + qb * MQ + 8 * g4 + 4 * hh);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int it = 4 * g4 + j;
+                            const int off = 8 * g4 + j;
+                            float p = fast_exp2(__builtin_fmaf(s[it], a.c, -l4[j] * kLog2e));
+                            if constexpr (MASKED) {
+                                bool drop = (off + rel < 0) | (rs + (uint32_t)off + 4u * hh >= a.len);
+                                if constexpr (WIN) drop = drop | (off + rel >= (int)a.window);
+                                p = drop ? 0.f : p;
+                            }
+                            pv[4 * g2 + j] = p;
+                            dv8[4 * g2 + j] = p * (dp[it] - d4[j]);
+                        }
+                    }
+                    split_bf16(pv, pf[cc], pl[cc]);
+                    split_bf16(dv8, dsf[cc], dsl[cc]);
+                }
+            };
+            const bool edge = rs < kw0 + MQ || rs + MQ > a.len || (WIN && rs + MQ - 1 >= kw0 + a.window);
+            if (edge) probs(std::true_type{});
+            else probs(std::false_type{});
+            // dV^T += dO^T P,  dK^T += Q^T dS
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) {
+                    dvt[db] = mfma(ot8[db][cc], pf[cc], dvt[db]);
+                    dvt[db] = mfma(ot8[db][cc], pl[cc], dvt[db]);
+                    dkt[db] = mfma(qt8[db][cc], dsf[cc], dkt[db]);
+                    dkt[db] = mfma(qt8[db][cc], dsl[cc], dkt[db]);
                 }
         }
     }
