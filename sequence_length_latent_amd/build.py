@@ -5,12 +5,16 @@
 Compiles every source under ``csrc/`` with hipcc for gfx950 only and links
 ``sequence_length_latent_amd/_hd_sfa.so``.  Objects go to ``_build/`` at the
 repository root.  Packed-fp32 instructions are disabled for all device code.
+The compiler's resource report of every kernel (registers, scratch, LDS,
+occupancy) is written next to the library as ``_hd_sfa.resources.json``.
 """
 from __future__ import annotations
 
 import concurrent.futures as cf
 import glob
+import json
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -21,6 +25,13 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "_hd_sfa.so")
+RESOURCES = os.path.join(PKG, "_hd_sfa.resources.json")
+_REMARK = "-Rpass-analysis=kernel-resource-usage"
+_FIELDS = {"vgpr": r"VGPRs: (\d+)", "agpr": r"AGPRs: (\d+)", "sgpr": r"SGPRs: (\d+)",
+           "scratch_bytes_per_lane": r"ScratchSize \[bytes/lane\]: (\d+)",
+           "vgpr_spill": r"VGPRs Spill: (\d+)", "sgpr_spill": r"SGPRs Spill: (\d+)",
+           "lds_bytes": r"LDS Size \[bytes/block\]: (\d+)",
+           "occupancy_waves_per_simd": r"Occupancy \[waves/SIMD\]: (\d+)"}
 
 ARCH = "gfx950"
 CFLAGS = [
@@ -38,17 +49,30 @@ def hipcc() -> str:
     return path
 
 
-def _compile(src: str) -> str:
+def _resources(report: str) -> dict:
+    """Kernel name -> resource fields, from the compiler's resource remarks."""
+    out = {}
+    for chunk in report.split("Function Name: ")[1:]:
+        name = chunk.split()[0]
+        out[name] = {k: int(m.group(1)) for k, pat in _FIELDS.items() if (m := re.search(pat, chunk))}
+    return out
+
+
+def _compile(src: str):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *CFLAGS, "-c", src, "-o", obj]
+    device = src.endswith(".hip")
+    cmd = [hipcc(), *CFLAGS, *([_REMARK] if device else []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
+    lines = [l for l in (r.stderr or "").splitlines() if noise not in l]
+    remarks = "\n".join(l for l in lines if "remark:" in l)
+    # a remark is followed by its source line and a caret line ("  12 | ...", "     | ^")
+    err = "\n".join(l for l in lines if "remark:" not in l and not re.match(r"^\s*\d*\s*\|", l))
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{err}")
     if err.strip():
         print(err, file=sys.stderr)
-    return obj
+    return obj, _resources(remarks)
 
 
 def build(verbose: bool = True) -> str:
@@ -58,13 +82,20 @@ def build(verbose: bool = True) -> str:
     if not srcs:
         raise RuntimeError("no sources under csrc/")
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
+        done = list(ex.map(_compile, srcs))
+    objs = [o for o, _ in done]
+    resources = {}
+    for _, res in done:
+        resources.update(res)
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
     os.replace(tmp, LIB)
+    with open(RESOURCES + ".tmp", "w") as f:
+        json.dump(resources, f, indent=1, sort_keys=True)
+    os.replace(RESOURCES + ".tmp", RESOURCES)
     if verbose:
         print(f"built {LIB} from {len(srcs)} sources")
     return LIB

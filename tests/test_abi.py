@@ -236,3 +236,26 @@ def test_product_path_does_not_import_the_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
+
+
+def test_no_kernel_spills_to_scratch():
+    """Every kernel of the library keeps its working set in registers and LDS:
+    no scratch memory and no VGPR spills (from the compiler's resource report
+    that the build writes next to the library).  SGPR spills are allowed: with
+    no scratch they go to lanes of a VGPR (the prefill kernels park the
+    diagonal tile's hoisted lane masks there, read once per work item)."""
+    import json
+    import os
+    from sequence_length_latent_amd import build as b
+    assert os.path.exists(b.RESOURCES), "build the library first (python -m sequence_length_latent_amd.build)"
+    res = json.load(open(b.RESOURCES))
+    kernels = [k for k in res if "_kernel" in k]
+    # every kernel family of the path is reported
+    for fam in ("expand_kernel", "sfa_prefill_kernel", "decode_append_kernel", "decode_attend_kernel",
+                "decode_combine_kernel", "rowcopy_kernel", "dq_kernel", "dkv_kernel"):
+        assert any(fam in k for k in kernels), fam
+    for k in kernels:
+        r = res[k]
+        assert r.get("scratch_bytes_per_lane", 0) == 0, (k, r)
+        assert r.get("vgpr_spill", 0) == 0, (k, r)
+        assert r.get("lds_bytes", 0) <= 160 * 1024, (k, r)
