@@ -268,19 +268,32 @@ def bench_decode_stack(args, torch, hd, si):
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / reps
+        # the same step recorded as one HIP graph and replayed
+        graph = st.capture(qs, ks, vs, tb, T, D ** -0.5, outs, ws)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_graph = e0.elapsed_time(e1) / reps
+        del graph
         entry = Hkv * D * 2 * 2
         nbytes = sum(S * ((W + n - 1) if k == sch.SLIDING else (T + 1) * n) * entry for k in kinds)
         res[name] = {"layers": len(kinds), "counts": sch.SCHEDULES[name], "ms_per_step": round(ms, 3),
                      "bytes_per_step": nbytes, "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1),
                      "unit": "GB/s", "peak": PEAK_HBM_GBS,
                      "frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                     "tokens_per_s": round(S / (ms * 1e-3), 1)}
+                     "tokens_per_s": round(S / (ms * 1e-3), 1),
+                     "ms_per_step_graph": round(ms_graph, 3)}
         del st, qs, ks, vs, outs, ws
         torch.cuda.empty_cache()
     res["workload"] = (f"{S} sequences x {T} tokens x {n} streams cached, {Hq}/{Hkv} heads, head_dim {D}, "
                        f"pages of {P} entries, sliding window {W} positions; one decode step of every "
                        "attention layer (append + attention + combine per layer); tokens_per_s counts one "
-                       "token per sequence per step, attention only")
+                       "token per sequence per step, attention only; ms_per_step_graph: the same step "
+                       "replayed as one captured HIP graph")
     return res
 
 

@@ -88,3 +88,16 @@ class PagedDecodeStack:
                               self.page_table, tokens_before, self.n, max_tokens, mode, scale,
                               window=window, workspace=workspace, out=outs[i])
         return outs
+
+    def capture(self, q_new, k_new, v_new, tokens_before, max_tokens, scale, outs, workspace):
+        """Record one decode step of every layer (append, attention and, where a
+        view has several splits, combine: up to 3 kernels per layer) as a HIP
+        graph over these buffers.  ``graph.replay()`` then runs the whole step
+        with one host call on whatever the buffers hold at that time (the next
+        token's rows in q_new / k_new / v_new, the next tokens_before, a changed
+        page table).  The step launches kernels only (no memory fills), and
+        allocates nothing given ``outs`` and ``workspace``."""
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.step(q_new, k_new, v_new, tokens_before, max_tokens, scale, outs, workspace)
+        return graph

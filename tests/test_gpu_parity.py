@@ -760,6 +760,55 @@ def test_decode_paged_oracle_on_gathered_pages():
     assert_close(f64(out), ref, "paged decode vs oracle")
 
 
+def test_decode_stack_graph_replays_match_eager():
+    """The layer-schedule step recorded as a HIP graph: three replays, each on
+    new rows and new cache lengths written into the captured buffers, with an
+    eager step between them, give the eager step's outputs and pools bit for bit."""
+    from sequence_length_latent_amd import schedule as sch
+    S, n, Hq, Hkv, D, P, T, W = 3, 4, 16, 4, 128, 16, 60, 90
+    kinds = [sch.WITHIN_STREAM, sch.SLIDING, sch.FULL]
+    mp = -(-((T + 1) * n) // P)
+    g = torch.Generator().manual_seed(7600)
+    pt = torch.randperm(S * mp + 3, generator=g)[: S * mp].reshape(S, mp).to(torch.int32).to(DEV)
+    st = sch.PagedDecodeStack(kinds, S, n, Hq, Hkv, D, P, mp, W, device=DEV, page_table=pt,
+                              num_pages=S * mp + 3)
+    for i in range(len(kinds)):
+        st.k_pools[i].copy_(_rand(st.k_pools[i].shape, 1.0, 7610 + i))
+        st.v_pools[i].copy_(_rand(st.v_pools[i].shape, 1.0, 7620 + i))
+    qs = [torch.empty((S, n, Hq, D), dtype=torch.bfloat16, device=DEV) for _ in kinds]
+    ks = [torch.empty((S, n, Hkv, D), dtype=torch.bfloat16, device=DEV) for _ in kinds]
+    vs = [torch.empty((S, n, Hkv, D), dtype=torch.bfloat16, device=DEV) for _ in kinds]
+    tb = torch.zeros(S, dtype=torch.int32, device=DEV)
+    outs = [torch.empty_like(q) for q in qs]
+    ws = st.workspace(T)
+
+    def fill(r):
+        for i in range(len(kinds)):
+            qs[i].copy_(_rand(qs[i].shape, 1.0, 7700 + 10 * r + i))
+            ks[i].copy_(_rand(ks[i].shape, 1.0, 7800 + 10 * r + i))
+            vs[i].copy_(_rand(vs[i].shape, 1.0, 7900 + 10 * r + i))
+        tb.copy_(torch.tensor([[60, 5, 33], [12, 60, 0], [59, 1, 47]][r], dtype=torch.int32))
+
+    fill(0)
+    graph = st.capture(qs, ks, vs, tb, T, D ** -0.5, outs, ws)
+    torch.cuda.synchronize()
+    for r in range(3):
+        fill(r)
+        before = [(kp.clone(), vp.clone()) for kp, vp in zip(st.k_pools, st.v_pools)]
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [o.clone() for o in outs]
+        got_pools = [(kp.clone(), vp.clone()) for kp, vp in zip(st.k_pools, st.v_pools)]
+        for (kp, vp), (kb, vb) in zip(zip(st.k_pools, st.v_pools), before):
+            kp.copy_(kb)
+            vp.copy_(vb)
+        st.step(qs, ks, vs, tb, T, D ** -0.5, outs, ws)
+        torch.cuda.synchronize()
+        for i in range(len(kinds)):
+            assert torch.equal(got[i].view(torch.int16), outs[i].view(torch.int16)), (r, i)
+            assert torch.equal(got_pools[i][0], st.k_pools[i]) and torch.equal(got_pools[i][1], st.v_pools[i])
+
+
 def test_decode_stack_three_layer_kinds():
     """A paged multi-layer decode step (within-stream, sliding-window and full
     mixing layers sharing one page table), each layer against the oracle."""
