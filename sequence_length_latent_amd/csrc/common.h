@@ -39,11 +39,6 @@ __device__ __forceinline__ float fast_exp2(float x) {
     return __builtin_amdgcn_exp2f(x);
 }
 
-// Exchange with the lane 32 positions away (the other half of the wave).
-__device__ __forceinline__ float xor32(float x) {
-    return __shfl_xor(x, 32, kWave);
-}
-
 // max / sum of x over lanes l and l^32, in registers (v_permlane32_swap):
 // swapping the upper half of one copy with the lower half of another leaves
 // lane l holding both x[l % 32] and x[l % 32 + 32].
