@@ -656,6 +656,20 @@ def test_decode_small_ragged(mode):
 
 
 @pytest.mark.parametrize("mode", [WITHIN, MIX])
+def test_decode_first_token_empty_caches(mode):
+    """The first decode step: every cache is empty (max_tokens 0), so token 0's
+    n rows are appended and attend to themselves only (mixing: stream s sees
+    streams 0..s of token 0; within-stream: each sees its own row, out = v)."""
+    out = _decode_case(si.DECODE, S=4, T=0, tb=[0, 0, 0, 0], mode=mode)
+    if mode == WITHIN:
+        cfg = si.DECODE
+        _, kn, vn, _, _, _ = si.decode_inputs(cfg, device=DEV, S=4, T=0, tokens_before=[0, 0, 0, 0])
+        G = cfg.Hq // cfg.Hkv
+        want = vn.repeat_interleave(G, dim=2)
+        assert torch.equal(out.view(torch.int16), want.view(torch.int16))
+
+
+@pytest.mark.parametrize("mode", [WITHIN, MIX])
 def test_decode_other_shapes(mode):
     # n=3 (not a power of two), G=8 -> 24 rows; D=64
     cfg = si.DecodeCfg("d3", 9, S=3, n=3, T=200, Hq=16, Hkv=2, D=64, scale=0.125)
