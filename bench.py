@@ -408,7 +408,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs the SFA hot path on a single "
+        print("bench.py measures one GPU only: the library runs the SFA hot path on a single "
               "MI355X (no collectives); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
