@@ -9,9 +9,12 @@
 // copies of the existing ones (new table s = old table s mod n_old).
 //
 // Both are HBM-bound row copies.  One kernel walks the destination in 16-byte
-// chunks (coalesced stores, whole 16-byte pieces of each source row) with
-// UNROLL independent loads in flight per thread; the source row of each
-// destination row is the only difference between the two operations.
+// chunks (coalesced stores, whole 16-byte pieces of each source row), one
+// chunk per thread, with nontemporal loads and stores (the data is touched
+// once: keeping it out of the caches measured 12% faster than cached
+// accesses with four chunks per thread, 6.5 vs 5.7 TB/s on 2.5 GB); the source
+// row of each destination row is the only difference between the two
+// operations.
 #include "common.h"
 
 namespace hdsfa {
@@ -19,7 +22,7 @@ namespace hdsfa {
 namespace {
 
 constexpr int kCopyThreads = 256;
-constexpr int kCopyUnroll = 4;
+constexpr int kCopyUnroll = 1;
 
 // FINAL: destination row r = b*L + t reads source row b*n*L + t*n + n-1
 //        (a = L, b = n).
@@ -51,16 +54,16 @@ rowcopy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                 const uint32_t bb = r / a;
                 const uint32_t t = r - bb * a;
                 const uint64_t srow = ((uint64_t)bb * a + t) * b + (b - 1);
-                val[u] = s[srow * cpr + w];
+                val[u] = __builtin_nontemporal_load(s + srow * cpr + w);
             } else {
-                val[u] = s[c];
+                val[u] = __builtin_nontemporal_load(s + c);
             }
         }
     }
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u) {
         const uint32_t c = base + (uint32_t)u * kCopyThreads;
-        if (c < chunks) d[c] = val[u];
+        if (c < chunks) __builtin_nontemporal_store(val[u], d + c);
     }
 }
 
