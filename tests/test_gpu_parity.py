@@ -759,6 +759,23 @@ def test_decode_paged_equals_contiguous(P, mode, window):
     assert np.array_equal(si.bits(kp), want)
 
 
+@pytest.mark.parametrize("n,Hq,Hkv,D,mode,P", [(8, 64, 8, 128, MIX, 32),     # 64 query rows
+                                                (8, 64, 8, 128, WITHIN, 32),
+                                                (3, 16, 2, 64, MIX, 8),        # head_dim 64
+                                                (3, 16, 2, 64, WITHIN, 64)])
+def test_decode_paged_other_shapes(n, Hq, Hkv, D, mode, P):
+    """Paged decode with 64 query rows per KV head (two 32-row blocks) and with
+    head_dim 64: bitwise the contiguous decode on the same rows."""
+    cfg = si.DecodeCfg("dpo", 15, S=3, n=n, T=150, Hq=Hq, Hkv=Hkv, D=D, scale=D ** -0.5)
+    tb = [150, 17, 0]
+    qn, kn, vn, kc, vc, tbt = si.decode_inputs(cfg, device=DEV, S=3, T=150, tokens_before=tb)
+    kp, vp, pt = _paged_from(kc, vc, P, 7150 + n + D + mode)
+    ref = hd.decode_step(qn, kn, vn, kc, vc, tbt, n, 150, mode, cfg.scale)
+    got = hd.decode_step_paged(qn, kn, vn, kp, vp, pt, tbt, n, 150, mode, cfg.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(ref.view(torch.int16), got.view(torch.int16))
+
+
 def test_decode_paged_oracle_on_gathered_pages():
     """Paged decode against the oracle on the rows gathered back through the
     page table (page size 32, mixing with a window)."""
