@@ -1,4 +1,5 @@
-// Stream-Factorized Attention, gradients of a prefill layer (sfa_attn_bwd).
+// Stream-Factorized Attention, gradients of a prefill layer (sfa_attn_bwd,
+// sfa_attn_bwd_window).
 //
 // "Hidden Decoding at Scale" review, sections Method and Results: the model
 // is trained on the length-nL sequence with the within-stream / mixing

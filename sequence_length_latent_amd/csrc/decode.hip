@@ -1,5 +1,6 @@
 // Hidden Decoding decode step over the retained per-stream KV cache
-// (sfa_decode_workspace_size, sfa_decode_step).
+// (sfa_decode_workspace_size, sfa_decode_step, sfa_decode_step_window,
+// sfa_decode_step_paged).
 //
 // "Hidden Decoding at Scale" review, sections Method and Limitations: the KV
 // of every stream is kept, so the cache holds n entries per token and later

@@ -1,4 +1,6 @@
-// Stream-Factorized Attention, prefill (sfa_stream_attn, sfa_mix_attn).
+// Stream-Factorized Attention, prefill (sfa_stream_attn, sfa_mix_attn,
+// sfa_mix_attn_window, and the training forwards sfa_attn_fwd and
+// sfa_attn_fwd_window, which also write each row's log-sum-exp).
 //
 // "Hidden Decoding at Scale" review, section Method: most layers attend only
 // within their own stream (cost of order n*L^2), a few mix streams with the
