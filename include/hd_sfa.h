@@ -44,8 +44,9 @@ typedef enum hd_status {
     HD_OK = 0,
     HD_ERR_NULL = 1,         /* a required pointer is NULL                       */
     HD_ERR_SHAPE = 2,        /* a size is negative/zero where it must not be,
-                                Hq is not a multiple of Hkv, or a pointer is
-                                misaligned                                        */
+                                Hq is not a multiple of Hkv, a pointer is
+                                misaligned, or a softmax scale is not finite
+                                and positive                                      */
     HD_ERR_UNSUPPORTED = 3,  /* head_dim other than 64/128, or a size beyond the
                                 library's 32-bit index range                     */
     HD_ERR_CAPACITY = 4,     /* KV cache too small for the appended entries      */
@@ -125,6 +126,8 @@ hd_status hd_cyclic_replicate(const uint16_t* tables, int32_t n_old, int64_t V, 
  *   q, out   bf16 [B, n*L, Hq, D]
  *   k, v     bf16 [B, n*L, Hkv, D]
  *   D        64 or 128; Hq a multiple of Hkv
+ *   softmax_scale  finite and > 0 (HD_ERR_SHAPE otherwise), as for every
+ *            attention entry point of this library
  * Scores, softmax statistics and the output accumulator are fp32; the two
  * contractions run on bf16 matrix cores; out is rounded to nearest even.
  * Work skipped: only token tiles of the query's own stream that are not in

@@ -504,6 +504,7 @@ hd_status launch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                      int64_t window = 0) {
     // window: 0 = plain causal, else >= 1 (mixing only; checked by the caller)
     if (B < 0 || L < 0 || n < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return HD_ERR_SHAPE;
+    if (!scale_ok(scale)) return HD_ERR_SHAPE;
     if (mode != 0 && mode != 1) return HD_ERR_SHAPE;
     if (D != 64 && D != 128) return HD_ERR_UNSUPPORTED;
     if (B == 0 || L == 0) return HD_OK;

@@ -72,6 +72,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
+// The kernels mask scores with -inf and track the running max of the raw
+// scores times the scale: both need a finite, positive softmax scale.
+inline bool scale_ok(float scale) {
+    return scale > 0.f && scale <= 3.4e38f;
+}
+
 inline bool aligned16(const void* p) {
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }

@@ -543,6 +543,7 @@ hd_status decode_step(const uint16_t* q_new, const uint16_t* k_new, const uint16
                       const Paging& pg = Paging{}) {
     const bool paged = pg.page_table != nullptr;
     if (S < 0 || n < 1 || Hq < 1 || Hkv < 1 || max_tokens < 0 || C_max < 0) return HD_ERR_SHAPE;
+    if (!scale_ok(softmax_scale)) return HD_ERR_SHAPE;
     if (Hq % Hkv != 0) return HD_ERR_SHAPE;
     if (mode != 0 && mode != 1) return HD_ERR_SHAPE;
     if (!decode_sizes_ok(S, n, Hq, Hkv, D, max_tokens)) return HD_ERR_UNSUPPORTED;

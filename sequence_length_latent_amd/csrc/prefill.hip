@@ -616,6 +616,7 @@ hd_status launch_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v
                          bool within, int64_t window, float* lse = nullptr) {
     // window: 0 = none (plain causal), else >= 1 rows of the view
     if (B < 0 || L < 0 || n < 1 || Hq < 1 || Hkv < 1 || window < 0) return HD_ERR_SHAPE;
+    if (!scale_ok(scale)) return HD_ERR_SHAPE;
     if (Hq % Hkv != 0) return HD_ERR_SHAPE;
     if (D != 64 && D != 128) return HD_ERR_UNSUPPORTED;
     if (B == 0 || L == 0) return HD_OK;

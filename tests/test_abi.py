@@ -259,3 +259,25 @@ def test_no_kernel_spills_to_scratch():
         assert r.get("scratch_bytes_per_lane", 0) == 0, (k, r)
         assert r.get("vgpr_spill", 0) == 0, (k, r)
         assert r.get("lds_bytes", 0) <= 160 * 1024, (k, r)
+
+
+def test_softmax_scale_must_be_finite_and_positive(lib):
+    """The kernels mask with -inf and track the max of raw scores times the
+    scale, so every attention entry point rejects a scale that is zero,
+    negative, infinite or NaN before any launch."""
+    bad = (0.0, -0.125, float("inf"), float("nan"))
+    args8 = [FAKE] * 8
+    for sc in bad:
+        assert lib.sfa_stream_attn(FAKE, FAKE, FAKE, FAKE, 1, 2, 8, 4, 2, 128, sc, None) == SHAPE
+        assert lib.sfa_mix_attn(FAKE, FAKE, FAKE, FAKE, 1, 2, 8, 4, 2, 128, sc, None) == SHAPE
+        assert lib.sfa_mix_attn_window(FAKE, FAKE, FAKE, FAKE, 1, 2, 8, 4, 2, 128, sc, 4, None) == SHAPE
+        assert lib.sfa_attn_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 8, 4, 2, 128, sc, 1, None) == SHAPE
+        assert lib.sfa_attn_fwd_window(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 8, 4, 2, 128, sc, 4, None) == SHAPE
+        assert lib.sfa_attn_bwd(*args8, 1, 2, 8, 4, 2, 128, sc, 1, FAKE, 1 << 20, None) == SHAPE
+        assert lib.sfa_attn_bwd_window(*args8, 1, 2, 8, 4, 2, 128, sc, 4, FAKE, 1 << 20, None) == SHAPE
+        assert lib.sfa_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 8, 2, 128, 44, 10, 1, sc,
+                                   FAKE, 1 << 30, FAKE, None) == SHAPE
+        assert lib.sfa_decode_step_window(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 8, 2, 128, 44, 10, 8, sc,
+                                          FAKE, 1 << 30, FAKE, None) == SHAPE
+        assert lib.sfa_decode_step_paged(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 8, 2, 128, 16, 64, 8,
+                                         10, 1, 0, sc, FAKE, 1 << 30, FAKE, None) == SHAPE
