@@ -229,9 +229,31 @@ dq_kernel(const BwdArgs a) {
                     st[kb] = mfma(lds16(kt + kb * 32 * ROWB + doff[e]), qf[e], st[kb]);
                     dpt[kb] = mfma(lds16(vt + kb * 32 * ROWB + doff[e]), dof[e], dpt[kb]);
                 }
-            // P^T = 2^(c s - lse2), masked past the query (and before its window)
+            // P^T = 2^(c s - lse2), masked past the query (and before its
+            // window).  The masks are applied to the scores (-inf, so P = 0:
+            // the scale is positive) and only on the wave's diagonal tile and
+            // (WIN) on tiles reaching below some row's window; the other tiles
+            // carry no mask work.
             const int rel = (int)qi - m * BN - 4 * hh;
             const bool diag = m == last;
+            if (diag) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int it = 0; it < 16; ++it) {
+                        const int off = kb * 32 + 8 * (it >> 2) + (it & 3);
+                        if (off > rel) st[kb][it] = -INFINITY;
+                    }
+            }
+            if (WIN && (uint32_t)m * BN + a.window <= q0 + MQ - 1) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int it = 0; it < 16; ++it) {
+                        const int off = kb * 32 + 8 * (it >> 2) + (it & 3);
+                        if (off <= rel - (int)a.window) st[kb][it] = -INFINITY;   // key before the window
+                    }
+            }
             bf16x8 dsf[4], dsl[4];
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) {
@@ -239,10 +261,7 @@ dq_kernel(const BwdArgs a) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int kb = cc >> 1, it = (cc & 1) * 8 + j;
-                    const int off = kb * 32 + 8 * (it >> 2) + (it & 3);
-                    float p = fast_exp2(__builtin_fmaf(st[kb][it], a.c, -lse2));
-                    if (diag && off > rel) p = 0.f;
-                    if (WIN && off <= rel - (int)a.window) p = 0.f;       // key before the window
+                    const float p = fast_exp2(__builtin_fmaf(st[kb][it], a.c, -lse2));
                     if constexpr (SECOND) v8[j] = p * (dpt[kb][it] - dl);   // dS^T
                     else dsum[j & 3] = __builtin_fmaf(p, dpt[kb][it], dsum[j & 3]);
                 }
