@@ -236,6 +236,25 @@ def bench_decode(args, torch, hd, si):
     res["cfg"] = cfg
     del qn, kn, vn, kc, vc, tb, ws, out
     torch.cuda.empty_cache()
+    # long context: one layer over 32 sequences x 32768 tokens x 4 streams
+    lc = si.DECODE_LONG
+    qn, kn, vn, kc, vc, tb = si.decode_inputs(lc, device=dev)
+    ws = torch.empty(hd.decode_workspace_size(lc.S, lc.n, lc.Hq, lc.Hkv, lc.D, lc.T),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty_like(qn)
+    lreps = max(2, args.steps // 4)
+    for mode, name in ((0, "long_within"), (1, "long_mix")):
+        for _ in range(2):
+            hd.decode_step(qn, kn, vn, kc, vc, tb, lc.n, lc.T, mode, lc.scale, ws, out)
+        e0.record()
+        for _ in range(lreps):
+            hd.decode_step(qn, kn, vn, kc, vc, tb, lc.n, lc.T, mode, lc.scale, ws, out)
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / lreps
+    res["bytes_long"] = decode_bytes(lc.S, lc.n, lc.T, lc.Hkv, lc.D)
+    del qn, kn, vn, kc, vc, tb, ws, out
+    torch.cuda.empty_cache()
     return res
 
 
@@ -539,6 +558,15 @@ def main():
             "bytes_per_call": dec["bytes_window"],
             "note": "sliding-window mixing decode: K+V of the last window + n - 1 entries per "
                     "sequence; not part of the step"}
+        line["decode"]["long_context"] = {
+            "workload": "one layer over 32 sequences x 32768 tokens x 4 streams cached (131076 live "
+                        "entries after the append, 17.2 GB of K+V), 32/8 heads, head_dim 128",
+            "bytes_per_call": dec["bytes_long"]}
+        for name, key in (("within", "long_within"), ("mix", "long_mix")):
+            gbs = dec["bytes_long"] / (dec[key] * 1e-3) / 1e9
+            line["decode"]["long_context"][name] = {"ms": round(dec[key], 4), "achieved": round(gbs, 1),
+                                                    "unit": "GB/s", "peak": PEAK_HBM_GBS,
+                                                    "frac": round(gbs / PEAK_HBM_GBS, 4)}
         line["decode"]["traffic"] = measured_traffic("decode_attend_kernel", "decode.hip")
     if stack:
         line["stack"] = stack

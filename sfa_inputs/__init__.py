@@ -92,6 +92,11 @@ LONG = PrefillCfg("long", 4, n=4, B=1, L=8192, Hq=64, Hkv=4, D=128,
                   layers=("within", "mix"))
 DECODE = DecodeCfg("decode", 5, S=64, n=4, T=4096, Hq=32, Hkv=8, D=128,
                    scale=1 / math.sqrt(128))
+# long context: 32 sequences x 32768 tokens x 4 streams (a 17.2 GB K+V cache
+# for one layer); the 32k-input, batch-32 serving point is where the Hidden
+# Decoding serving matrix (Figure 5, Limitations) shows the largest decode cost
+DECODE_LONG = DecodeCfg("decode_long", 6, S=32, n=4, T=32768, Hq=32, Hkv=8, D=128,
+                        scale=1 / math.sqrt(128))
 
 PREFILL_CFGS = (TINY, N4, N8STACK, LONG)
 

@@ -686,6 +686,32 @@ def test_decode_full_size_sampled(mode):
     _decode_case(cfg, S=cfg.S, T=cfg.T, tb=None, mode=mode, seqs=[0, 31, 63])
 
 
+@pytest.mark.parametrize("mode", [WITHIN, MIX])
+def test_decode_long_context_sampled(mode):
+    """Long-context decode at full size: 32 sequences x 32768 tokens x 4
+    streams (a 17.2 GB K+V cache), ragged token counts, in the launch the
+    bench times; two sequences checked against the oracle (each ~131k
+    entries), the appends of those sequences bit-exact."""
+    cfg = si.DECODE_LONG
+    tb = [cfg.T - (i * 1031) % 4096 for i in range(cfg.S)]
+    qn, kn, vn, kc, vc, tbt = si.decode_inputs(cfg, device=DEV, tokens_before=tb)
+    seqs = [0, 19]
+    before = {qi: (si.bits(kc[qi:qi + 1]), si.bits(vc[qi:qi + 1])) for qi in seqs}
+    out = hd.decode_step(qn, kn, vn, kc, vc, tbt, cfg.n, cfg.T, mode, cfg.scale)
+    torch.cuda.synchronize()
+    tbh = np.asarray(tb, dtype=np.int32)
+    for qi in seqs:
+        sl = slice(qi, qi + 1)
+        k2, v2 = oracle.decode_append_ref(before[qi][0], before[qi][1], si.bits(kn[sl]),
+                                          si.bits(vn[sl]), tbh[sl], cfg.n)
+        assert np.array_equal(si.bits(kc[sl]), k2), f"k append seq {qi}"
+        assert np.array_equal(si.bits(vc[sl]), v2), f"v append seq {qi}"
+        ref = oracle.decode_ref(si.bits(qn[sl]), k2, v2, tbh[sl], cfg.n, mode, cfg.scale)
+        assert_close(f64(out[sl]), ref, f"long decode seq {qi} T={tbh[qi]} mode={mode}")
+    del qn, kn, vn, kc, vc, tbt, out
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("window", [1, 3, 64, 129, 500, 1 << 20])
 def test_decode_window_ragged(window):
     """Sliding-window mixing decode over ragged caches (windows inside one
