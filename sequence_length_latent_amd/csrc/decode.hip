@@ -16,8 +16,9 @@
 //                  is needed.  Mixing mode: one view of all (T+1)*n entries
 //                  with n*G query rows, causal only among the n new entries.
 //                  Either way every cache byte is read exactly once per call.
-//                  K and V tiles are staged through LDS with coalesced loads
-//                  (V transposed for the V^T operand) and both contractions
+//                  K and V tiles are staged through LDS row-major with
+//                  coalesced loads (16 lanes per 256-byte row; the V^T
+//                  operand comes from transpose reads) and both contractions
 //                  run on v_mfma_f32_32x32x16_bf16; 4 waves take 32 keys each
 //                  of a 128-key tile and merge their (max, sum, O) at the end;
 //   3. combine  -- merges the per-split partials (fp32) into bf16 output
@@ -40,8 +41,13 @@ namespace {
 constexpr int DT = 128;            // keys per workgroup tile (32 per wave)
 constexpr int DNW = 4;             // waves
 constexpr int DTHREADS = DNW * kWave;
-constexpr int DVP = DT + 8;        // transposed-V pitch (elements)
 constexpr int kTargetBlocks = 512;    // split-plan target: two resident workgroups on each of 256 CUs
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+// an LDS address for the transpose read (the pointer points into __shared__ memory)
+__device__ __forceinline__ __attribute__((address_space(3))) v4i16* lds_v4(const uint16_t* p) {
+    return (__attribute__((address_space(3))) v4i16*)(p);
+}
 
 struct DecodeArgs {
     const uint16_t* q;         // [S, n, Hq, D]
@@ -76,11 +82,6 @@ __device__ __forceinline__ uint64_t paged_row(const int32_t* __restrict__ pt, ui
 __device__ __forceinline__ uint32_t view_start(uint32_t T, uint32_t n, uint32_t window) {
     const uint32_t p0 = T * n;
     return (window != 0u && p0 + 1u >= window) ? p0 + 1u - window : 0u;
-}
-
-__device__ __forceinline__ int vt_pos(int kq) {
-    const int qq = kq & 3;
-    return 16 * (kq >> 2) + ((qq & 1) << 3) + ((qq >> 1) << 2);
 }
 
 __device__ __forceinline__ uint32_t clamp_tokens(int32_t t, uint32_t max_tokens) {
@@ -131,11 +132,12 @@ decode_attend_kernel(const DecodeArgs a) {
     constexpr int DBLK = D / 32;
     constexpr int CPR = D / 8;
     constexpr int K_CHUNKS = DT * CPR / DTHREADS;
-    constexpr int V_TASKS = (DT / 4) * (D / 8);
-    constexpr int V_PER = V_TASKS / DTHREADS;
-    static_assert(V_TASKS % DTHREADS == 0, "tile/thread mismatch");
-    // LDS: K tile + transposed V tile; reused for the cross-wave merge
-    constexpr int TILE_ELEMS = KS_ELEMS + D * DVP;
+    static_assert((DT * CPR) % DTHREADS == 0, "tile/thread mismatch");
+    // V rows are padded to D + 32 elements: the 4 rows a 16-lane group reads
+    // in one transpose read then start 16 banks apart
+    constexpr int VP = D + 32;
+    // LDS: K tile + V tile (both row-major); reused for the cross-wave merge
+    constexpr int TILE_ELEMS = KS_ELEMS + DT * VP;
     constexpr int MERGE_FLOATS = DNW * NQB * 32 * D;
     constexpr int SMEM_BYTES = (TILE_ELEMS * 2 > MERGE_FLOATS * 4) ? TILE_ELEMS * 2 : MERGE_FLOATS * 4;
     __shared__ __attribute__((aligned(16))) unsigned char smem_raw[SMEM_BYTES];
@@ -144,7 +146,7 @@ decode_attend_kernel(const DecodeArgs a) {
     // PAGED: pool row of each key of the next two tiles (slot = tile parity)
     __shared__ uint32_t row_tab[PAGED ? 2 * DT : 1];
     uint16_t* ks = reinterpret_cast<uint16_t*>(smem_raw);
-    uint16_t* vt = ks + KS_ELEMS;
+    uint16_t* vs = ks + KS_ELEMS;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -207,6 +209,9 @@ decode_attend_kernel(const DecodeArgs a) {
 
     // Tiles go global -> registers -> LDS: the next tile (64 KB per
     // workgroup) is in flight while the current one is consumed from LDS.
+    // K and V use the same pattern: 16 consecutive lanes read one key's
+    // 256-byte row, so every load instruction covers whole rows (gathering
+    // 4 keys per lane for a register transpose of V instead cost 4-10%).
     // Rows past the split end are clamped to its last row: the mask below
     // gives them probability 0.
     // PAGED: the pool rows of a tile's keys come from row_tab, filled two
@@ -217,7 +222,7 @@ decode_attend_kernel(const DecodeArgs a) {
     // them would also drain the tile already in flight).
     struct TileRegs {
         u32x4 k[K_CHUNKS];
-        u32x4 v[V_PER][4];
+        u32x4 v[K_CHUNKS];
         int32_t pg;       // PAGED: raw page id of this thread's key of tile t+2
         uint32_t pg_lo;   //        and that key's slot within its page
     };
@@ -250,19 +255,14 @@ decode_attend_kernel(const DecodeArgs a) {
             }
         }
 #pragma unroll
-        for (int i = 0; i < V_PER; ++i) {
-            const int task = tid + i * DTHREADS;
-            const int kq = task % (DT / 4);
-            const int dq = task / (DT / 4);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if constexpr (PAGED) {
-                    const uint64_t row = tab[4 * kq + q];
-                    r.v[i][q] = *reinterpret_cast<const u32x4*>(a.vc + row * erow + (uint64_t)kvh * D + dq * 8);
-                } else {
-                    const uint32_t key = min(k0 + 4 * kq + q, last_key);
-                    r.v[i][q] = *reinterpret_cast<const u32x4*>(vbase + key * kstep + dq * 8);
-                }
+        for (int i = 0; i < K_CHUNKS; ++i) {
+            const int cidx = tid + i * DTHREADS;
+            if constexpr (PAGED) {
+                const uint64_t row = tab[cidx / CPR];
+                r.v[i] = *reinterpret_cast<const u32x4*>(a.vc + row * erow + (uint64_t)kvh * D + (cidx % CPR) * 8);
+            } else {
+                const uint32_t key = min(k0 + cidx / CPR, last_key);
+                r.v[i] = *reinterpret_cast<const u32x4*>(vbase + key * kstep + (cidx % CPR) * 8);
             }
         }
         if constexpr (PAGED) {
@@ -281,24 +281,23 @@ decode_attend_kernel(const DecodeArgs a) {
             *reinterpret_cast<u32x4*>(ks + row * KP + col * 8) = r.k[i];
         }
 #pragma unroll
-        for (int i = 0; i < V_PER; ++i) {
-            const int task = tid + i * DTHREADS;
-            const int kq = task % (DT / 4);
-            const int dq = task / (DT / 4);
-            const int pos = vt_pos(kq);
-            // transpose 4 keys x 8 dims: row d of V^T gets the 4 keys' element d
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                u32x2 lo = {__builtin_amdgcn_perm(r.v[i][1][w], r.v[i][0][w], 0x05040100u),
-                            __builtin_amdgcn_perm(r.v[i][3][w], r.v[i][2][w], 0x05040100u)};
-                u32x2 hi = {__builtin_amdgcn_perm(r.v[i][1][w], r.v[i][0][w], 0x07060302u),
-                            __builtin_amdgcn_perm(r.v[i][3][w], r.v[i][2][w], 0x07060302u)};
-                *reinterpret_cast<u32x2*>(vt + (dq * 8 + 2 * w) * DVP + pos) = lo;
-                *reinterpret_cast<u32x2*>(vt + (dq * 8 + 2 * w + 1) * DVP + pos) = hi;
-            }
+        for (int i = 0; i < K_CHUNKS; ++i) {
+            const int cidx = tid + i * DTHREADS;
+            const int row = cidx / CPR;
+            const int col = cidx % CPR;
+            *reinterpret_cast<u32x4*>(vs + row * VP + col * 8) = r.v[i];
         }
     };
 
+    // V^T operand of O^T += V^T P^T from the row-major V tile by transpose
+    // reads (ds_read_b64_tr_b16): the 16 lanes of group g = lane / 16 each
+    // address 4 dims (4 * (lane % 4)) of one of 4 key rows (lane % 16 / 4);
+    // lane i of the group receives dim 16 * (g % 2) + i of those 4 keys.
+    // Groups 0-1 take keys 0-3, groups 2-3 keys 4-7 of each 8-key half; the
+    // second read (+8 keys) completes the 8 k-slots, which then hold keys
+    // 4*hh + {0..3, 8..11} in the order the P^T operand holds them.
+    const uint16_t* vlane = vs + (wave * 32 + 4 * (lane >> 5) + ((lane & 15) >> 2)) * VP +
+                            16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     auto compute = [&](int t) {
         const uint32_t wk0 = key0 + (uint32_t)t * DT + wave * 32;   // this wave's first key
         if (wk0 >= key_end) return;
@@ -356,10 +355,13 @@ decode_attend_kernel(const DecodeArgs a) {
         }
 #pragma unroll
         for (int db = 0; db < DBLK; ++db) {
-            const uint16_t* vrow = vt + (db * 32 + l32) * DVP + wave * 32 + hh * 8;
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-                const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vrow + 16 * c);
+                const uint16_t* src = vlane + (16 * c) * VP + 32 * db;
+                const v4i16 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4(src));
+                const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4(src + 8 * VP));
+                const u32x2 lo = __builtin_bit_cast(u32x2, lo4), hi = __builtin_bit_cast(u32x2, hi4);
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb)
                     oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][c], oacc[qb][db], 0, 0, 0);
