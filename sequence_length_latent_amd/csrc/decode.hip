@@ -489,19 +489,28 @@ struct SplitPlan {
     uint32_t nsplit, split;
 };
 
+// Splits of one view: about kTargetBlocks workgroups in all, whole tiles per
+// split.  The workspace stride is the larger full-view plan of the two modes;
+// a window plan is capped at the full mixing plan's split count, so it never
+// needs a wider stride (rounding splits up to whole tiles can otherwise give
+// a shorter window view more splits than the full view).
 SplitPlan plan_splits(uint64_t S, uint32_t n, uint32_t Hkv, uint64_t max_tokens, bool within,
                       uint64_t window = 0) {
-    uint64_t len_max = within ? max_tokens + 1 : (max_tokens + 1) * n;
-    if (!within && window != 0 && window + n - 1 < len_max) len_max = window + n - 1;
     const uint64_t units = S * Hkv * (within ? n : 1u);
-    uint64_t want = (kTargetBlocks + units - 1) / units;
-    const uint64_t max_splits = (len_max + DT - 1) / DT;
-    if (want > max_splits) want = max_splits;
-    if (want < 1) want = 1;
-    uint64_t split = (len_max + want - 1) / want;
-    split = (split + DT - 1) / DT * DT;
-    const uint64_t nsplit = (len_max + split - 1) / split;
-    return {(uint32_t)nsplit, (uint32_t)split};
+    auto make = [&](uint64_t len_max, uint64_t cap) -> SplitPlan {
+        uint64_t want = (kTargetBlocks + units - 1) / units;
+        const uint64_t max_splits = (len_max + DT - 1) / DT;
+        if (want > max_splits) want = max_splits;
+        if (want > cap) want = cap;
+        if (want < 1) want = 1;
+        uint64_t split = (len_max + want - 1) / want;
+        split = (split + DT - 1) / DT * DT;
+        const uint64_t nsplit = (len_max + split - 1) / split;
+        return {(uint32_t)nsplit, (uint32_t)split};
+    };
+    const SplitPlan full = make(within ? max_tokens + 1 : (max_tokens + 1) * n, ~0ull);
+    if (within || window == 0 || window + n - 1 >= (max_tokens + 1) * n) return full;
+    return make(window + n - 1, full.nsplit);
 }
 
 bool decode_sizes_ok(int64_t S, int32_t n, int32_t Hq, int32_t Hkv, int32_t D,

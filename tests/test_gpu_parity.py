@@ -680,6 +680,27 @@ def test_decode_other_shapes(mode):
 
 
 @pytest.mark.parametrize("mode", [WITHIN, MIX])
+def test_decode_many_streams(mode):
+    """Stream counts where a stream has several keys per 32-key wave slice
+    (n=5), or at most one (n=40 > 32), exercising the within-stream row mask."""
+    cfg = si.DecodeCfg("d5", 15, S=3, n=5, T=90, Hq=4, Hkv=2, D=64, scale=0.11)
+    _decode_case(cfg, S=3, T=90, tb=[90, 41, 0], mode=mode)
+    cfg = si.DecodeCfg("d40", 16, S=2, n=40, T=20, Hq=1, Hkv=1, D=128, scale=0.09)
+    _decode_case(cfg, S=2, T=20, tb=[20, 7], mode=mode)
+
+
+def test_decode_window_split_plan_capped():
+    """37 sequences x 2 KV heads (74 units, ~7 splits wanted), 250 tokens x 4
+    streams: the full view gets 4 splits of 256 entries, and a window of 797
+    would on its own get 7 splits of 128.  The window plan is capped at the
+    full view's split count (the workspace stride), so the partials of one
+    row never reach the next row's."""
+    cfg = si.DecodeCfg("dcap", 17, S=37, n=4, T=249, Hq=8, Hkv=2, D=128, scale=0.09)
+    tb = [249 - (i * 37) % 250 for i in range(37)]
+    _decode_case(cfg, S=37, T=249, tb=tb, mode=MIX, seqs=[0, 1, 18, 36], window=797)
+
+
+@pytest.mark.parametrize("mode", [WITHIN, MIX])
 def test_decode_full_size_sampled(mode):
     """Decode workload at full size: 64 sequences x 16384 cached entries."""
     cfg = si.DECODE
