@@ -75,7 +75,7 @@ int hd_abi_version(void);
  *                                   cleared: the caller zeroes it first); the n
  *                                   rows of such a token are written as zeros
  * Pure copy: the result is bit-identical to the gather.  H must be a multiple
- * of 8.
+ * of 8; B*L*n (output rows) must stay below 2^31 (HD_ERR_UNSUPPORTED).
  */
 hd_status hd_expand(const int32_t* ids, int64_t B, int64_t L,
                     const uint16_t* tables, int32_t n, int64_t V, int64_t H,

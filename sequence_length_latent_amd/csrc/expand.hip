@@ -5,10 +5,16 @@
 // every token becomes n streams, stream s taken from its own embedding table,
 // laid out as one length-nL sequence.  Position of (t, s) is t*n + s.
 //
-// HBM-bound gather: each output row is an H-element bf16 row of table s.  The
-// kernel walks the output in 16-byte chunks, so stores are fully coalesced and
-// every table row is read as whole 16-byte pieces.  Each thread keeps UNROLL
-// independent loads in flight before storing.
+// HBM-bound gather: one workgroup per output row (an H-element bf16 row of
+// table s).  The row's token id is one uniform (scalar) load, so the table
+// reads wait on a single short lookup; each thread then moves 16-byte chunks
+// with two loads in flight before its stores (fully coalesced, whole 16-byte
+// pieces of the table row).  Workgroups are ordered table-major, so the ones
+// that run together read one table's rows for different tokens rather than
+// the n rows of one token, which sit whole table sizes apart.  On cold
+// tables this is ~9% faster than walking the output in chunks with every
+// thread looking its id up itself (26.5 vs 29.2 us at 2 x 1024 tokens x 4
+// streams, hidden 4096).
 #include "common.h"
 
 namespace hdsfa {
@@ -16,36 +22,32 @@ namespace hdsfa {
 namespace {
 
 constexpr int kExpandThreads = 256;
-constexpr int kExpandUnroll = 4;
 
 __global__ void __launch_bounds__(kExpandThreads)
 expand_kernel(const int32_t* __restrict__ ids, const u32x4* __restrict__ tables,
               u32x4* __restrict__ out, int32_t* __restrict__ err_flag,
-              uint32_t n, uint32_t V, uint32_t chunks_per_row, uint32_t total_chunks) {
-    const uint32_t base = blockIdx.x * (kExpandThreads * kExpandUnroll) + threadIdx.x;
-    u32x4 val[kExpandUnroll];
-#pragma unroll
-    for (int u = 0; u < kExpandUnroll; ++u) {
-        const uint32_t c = base + (uint32_t)u * kExpandThreads;
-        val[u] = u32x4{0u, 0u, 0u, 0u};
-        if (c < total_chunks) {
-            // output row r = (b*L + t)*n + s, 16-byte chunk w inside the row
-            const uint32_t r = c / chunks_per_row;
-            const uint32_t w = c - r * chunks_per_row;
-            const uint32_t bt = r / n;
-            const uint32_t s = r - bt * n;
-            const int32_t tok = ids[bt];
-            if (tok >= 0 && (uint32_t)tok < V) {
-                val[u] = tables[((uint64_t)s * V + (uint32_t)tok) * chunks_per_row + w];
-            } else if (err_flag != nullptr) {
-                *err_flag = 1;
-            }
-        }
+              uint32_t n, uint32_t V, uint32_t chunks_per_row, uint32_t tokens) {
+    // workgroup i takes table s = i / tokens, token bt = i mod tokens (output
+    // row r = bt*n + s): workgroups that run together read rows of one table
+    // for different tokens
+    const uint32_t s = blockIdx.x / tokens;
+    const uint32_t bt = blockIdx.x - s * tokens;
+    const uint32_t r = bt * n + s;
+    const int32_t tok = ids[bt];
+    u32x4* dst = out + (uint64_t)r * chunks_per_row;
+    if (tok < 0 || (uint32_t)tok >= V) {
+        // out-of-range id: a zero row, and the error flag
+        for (uint32_t w = threadIdx.x; w < chunks_per_row; w += kExpandThreads) dst[w] = u32x4{0u, 0u, 0u, 0u};
+        if (threadIdx.x == 0 && err_flag != nullptr) *err_flag = 1;
+        return;
     }
-#pragma unroll
-    for (int u = 0; u < kExpandUnroll; ++u) {
-        const uint32_t c = base + (uint32_t)u * kExpandThreads;
-        if (c < total_chunks) out[c] = val[u];
+    const u32x4* src = tables + ((uint64_t)s * V + (uint32_t)tok) * chunks_per_row;
+    for (uint32_t w = threadIdx.x; w < chunks_per_row; w += 2 * kExpandThreads) {
+        const uint32_t w2 = w + kExpandThreads;
+        const u32x4 a = src[w];
+        const u32x4 b = w2 < chunks_per_row ? src[w2] : u32x4{0u, 0u, 0u, 0u};
+        dst[w] = a;
+        if (w2 < chunks_per_row) dst[w2] = b;
     }
 }
 
@@ -62,14 +64,13 @@ extern "C" hd_status hd_expand(const int32_t* ids, int64_t B, int64_t L,
     if (B == 0 || L == 0) return HD_OK;
     if (ids == nullptr || tables == nullptr || out == nullptr) return HD_ERR_NULL;
     if (H % 8 != 0 || !aligned16(tables) || !aligned16(out)) return HD_ERR_SHAPE;
-    // 32-bit chunk indices: the output may hold at most 2^32 - 2^10 16-byte chunks
+    // one workgroup per output row (grid limit 2^31 - 1); 32-bit chunk index in a row
     const uint64_t chunks_per_row = (uint64_t)H / 8;
-    const uint64_t total = (uint64_t)B * (uint64_t)L * (uint64_t)n * chunks_per_row;
-    const uint64_t per_block = (uint64_t)kExpandThreads * kExpandUnroll;
-    if (V > 0xffffffffLL || total > 0xffffffffULL - per_block) return HD_ERR_UNSUPPORTED;
-    const uint64_t blocks = (total + per_block - 1) / per_block;
-    expand_kernel<<<dim3((uint32_t)blocks), dim3(kExpandThreads), 0, stream>>>(
+    const uint64_t rows = (uint64_t)B * (uint64_t)L * (uint64_t)n;
+    if (V > 0xffffffffLL || rows > 0x7fffffffULL || chunks_per_row > 0x7fffffffULL)
+        return HD_ERR_UNSUPPORTED;
+    expand_kernel<<<dim3((uint32_t)rows), dim3(kExpandThreads), 0, stream>>>(
         ids, reinterpret_cast<const u32x4*>(tables), reinterpret_cast<u32x4*>(out),
-        err_flag, (uint32_t)n, (uint32_t)V, (uint32_t)chunks_per_row, (uint32_t)total);
+        err_flag, (uint32_t)n, (uint32_t)V, (uint32_t)chunks_per_row, (uint32_t)((uint64_t)B * L));
     return launch_status();
 }

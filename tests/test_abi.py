@@ -64,6 +64,8 @@ def test_expand_validation(lib):
     # zero work: OK without touching anything, even with NULL buffers
     assert lib.hd_expand(None, 0, 4, None, 2, 10, 8, None, None, None) == OK
     assert lib.hd_expand(None, 3, 0, None, 2, 10, 8, None, None, None) == OK
+    # one workgroup per output row: B*L*n must stay below 2^31
+    assert lib.hd_expand(FAKE, 1 << 16, 1 << 14, FAKE, 2, 10, 8, FAKE, None, None) == UNSUP
 
 
 @pytest.mark.parametrize("fn", ["sfa_stream_attn", "sfa_mix_attn"])
