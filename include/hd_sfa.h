@@ -23,8 +23,9 @@
  *     caller owns every buffer and the stream.
  *   - Arguments are validated on the host before anything is launched; an
  *     invalid call returns a non-zero hd_status and touches no memory.  Data
- *     that only the device can check (token ids) is reported through a device
- *     flag.  No C++ exception crosses this interface.
+ *     that only the device can check (token ids, decode token counts and page
+ *     ids) is reported through a device flag.  No C++ exception crosses this
+ *     interface.
  *   - A call whose total work is zero (B, L or S equal to 0) returns HD_OK
  *     without launching.
  */
@@ -293,12 +294,19 @@ size_t sfa_decode_workspace_size(int64_t S, int32_t n, int32_t Hq, int32_t Hkv,
  *   k_cache, v_cache bf16 [S, C_max, Hkv, D], entry order p = t*n + s
  *   tokens_before  int32 [S], device memory, 0 <= T <= max_tokens
  *                  (values outside that range are clamped into it on the
- *                  device, so no access leaves the cache)
+ *                  device, so no access leaves the cache, and reported
+ *                  through err_flag)
  *   max_tokens     host-side bound on tokens_before, sizes the grid
  *   C_max          must be >= (max_tokens + 1) * n, else HD_ERR_CAPACITY
  *   workspace      device scratch of at least sfa_decode_workspace_size()
  *                  bytes, else HD_ERR_WORKSPACE; contents need no init
  *   out            bf16 [S, n, Hq, D]
+ *   err_flag       int32 scalar in device memory, or NULL: if not NULL and
+ *                  some tokens_before value lies outside [0, max_tokens],
+ *                  *err_flag is set to 1 (never cleared: the caller zeroes
+ *                  it first).  Such a sequence is computed with the clamped
+ *                  count, so its rows are defined but not what the caller
+ *                  meant; the flag is how the caller learns of it.
  * Requires n * Hq / Hkv <= 64 query rows per KV head.
  */
 hd_status sfa_decode_step(const uint16_t* q_new, const uint16_t* k_new,
@@ -307,7 +315,7 @@ hd_status sfa_decode_step(const uint16_t* q_new, const uint16_t* k_new,
                           int64_t S, int32_t n, int32_t Hq, int32_t Hkv,
                           int32_t D, int64_t C_max, int64_t max_tokens,
                           int32_t mode, float softmax_scale, void* workspace,
-                          size_t workspace_bytes, uint16_t* out,
+                          size_t workspace_bytes, uint16_t* out, int32_t* err_flag,
                           hipStream_t stream);
 
 /*
@@ -320,7 +328,8 @@ hd_status sfa_decode_step(const uint16_t* q_new, const uint16_t* k_new,
  *   k_pages, v_pages  bf16 [num_pages, page_size, Hkv, D] pools
  *   page_table        int32 [S, max_pages_per_seq], device memory; ids outside
  *                     [0, num_pages) are clamped into it on the device (no
- *                     access leaves the pool)
+ *                     access leaves the pool) and, for the pages the step
+ *                     reads or writes, reported through err_flag
  *   page_size         a power of two (HD_ERR_SHAPE otherwise); the pool may
  *                     hold at most 2^32 rows (num_pages*page_size,
  *                     HD_ERR_UNSUPPORTED beyond)
@@ -334,7 +343,8 @@ hd_status sfa_decode_step(const uint16_t* q_new, const uint16_t* k_new,
  * live row through the table.  The result equals sfa_decode_step (or
  * sfa_decode_step_window) on the same rows laid out contiguously, bit for
  * bit.  Workspace size as sfa_decode_workspace_size(S, n, Hq, Hkv, D,
- * max_tokens).
+ * max_tokens).  err_flag as sfa_decode_step, also set for an out-of-range
+ * page id.
  */
 hd_status sfa_decode_step_paged(const uint16_t* q_new, const uint16_t* k_new,
                                 const uint16_t* v_new, uint16_t* k_pages, uint16_t* v_pages,
@@ -343,7 +353,7 @@ hd_status sfa_decode_step_paged(const uint16_t* q_new, const uint16_t* k_new,
                                 int32_t page_size, int64_t num_pages, int32_t max_pages_per_seq,
                                 int64_t max_tokens, int32_t mode, int64_t window,
                                 float softmax_scale, void* workspace, size_t workspace_bytes,
-                                uint16_t* out, hipStream_t stream);
+                                uint16_t* out, int32_t* err_flag, hipStream_t stream);
 
 /*
  * sfa_decode_step_window -- sfa_decode_step for a sliding-window mixing layer
@@ -363,7 +373,7 @@ hd_status sfa_decode_step_window(const uint16_t* q_new, const uint16_t* k_new,
                                  int64_t S, int32_t n, int32_t Hq, int32_t Hkv,
                                  int32_t D, int64_t C_max, int64_t max_tokens,
                                  int64_t window, float softmax_scale, void* workspace,
-                                 size_t workspace_bytes, uint16_t* out,
+                                 size_t workspace_bytes, uint16_t* out, int32_t* err_flag,
                                  hipStream_t stream);
 
 #ifdef __cplusplus

@@ -208,13 +208,22 @@ def decode_workspace_size(S: int, n: int, Hq: int, Hkv: int, D: int, max_tokens:
     return int(load().sfa_decode_workspace_size(S, n, Hq, Hkv, D, max_tokens))
 
 
+def _flag_ptr(err_flag):
+    if err_flag is None:
+        return None
+    _need(err_flag, "err_flag", torch.int32, 1)
+    return err_flag.data_ptr()
+
+
 def decode_step(q_new, k_new, v_new, k_cache, v_cache, tokens_before, n: int,
                 max_tokens: int, mode: int, scale: float, workspace=None, out=None,
-                window=None):
+                window=None, err_flag=None):
     """Append the n new stream positions and attend from them (mode WITHIN or
     MIX).  q_new [S, n, Hq, D]; k_new/v_new [S, n, Hkv, D]; caches
     [S, C, Hkv, D] (appended in place); tokens_before int32 [S] on the GPU.
-    ``window`` (mode MIX only): sliding window in interleaved positions."""
+    ``window`` (mode MIX only): sliding window in interleaved positions.
+    ``err_flag`` (int32, one element, zeroed by the caller) is set to 1 if a
+    tokens_before value lies outside [0, max_tokens]."""
     _need(q_new, "q_new", torch.bfloat16, 4)
     _need(k_new, "k_new", torch.bfloat16, 4)
     _need(v_new, "v_new", torch.bfloat16, 4)
@@ -247,24 +256,26 @@ def decode_step(q_new, k_new, v_new, k_cache, v_cache, tokens_before, n: int,
             q_new.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
             v_cache.data_ptr(), tokens_before.data_ptr(), S, n, Hq, Hkv, D, C, max_tokens,
             int(window), float(scale), workspace.data_ptr(),
-            workspace.numel() * workspace.element_size(), out.data_ptr(), _stream())
+            workspace.numel() * workspace.element_size(), out.data_ptr(), _flag_ptr(err_flag),
+            _stream())
         check("sfa_decode_step_window", st)
         return out
     st = load().sfa_decode_step(q_new.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
                                 k_cache.data_ptr(), v_cache.data_ptr(), tokens_before.data_ptr(),
                                 S, n, Hq, Hkv, D, C, max_tokens, int(mode), float(scale),
                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                                out.data_ptr(), _stream())
+                                out.data_ptr(), _flag_ptr(err_flag), _stream())
     check("sfa_decode_step", st)
     return out
 
 
 def decode_step_paged(q_new, k_new, v_new, k_pages, v_pages, page_table, tokens_before, n: int,
                       max_tokens: int, mode: int, scale: float, window=None, workspace=None,
-                      out=None):
+                      out=None, err_flag=None):
     """decode_step over paged caches: pools [num_pages, P, Hkv, D] (appended in
     place), page_table int32 [S, max_pages_per_seq] and tokens_before int32 [S]
-    on the GPU.  ``window`` (mode MIX only): sliding window in positions."""
+    on the GPU.  ``window`` (mode MIX only): sliding window in positions.
+    ``err_flag`` as decode_step, also set for a page id outside the pool."""
     for t, nm in ((q_new, "q_new"), (k_new, "k_new"), (v_new, "v_new"), (k_pages, "k_pages"),
                   (v_pages, "v_pages")):
         _need(t, nm, torch.bfloat16, 4)
@@ -292,6 +303,6 @@ def decode_step_paged(q_new, k_new, v_new, k_pages, v_pages, page_table, tokens_
         page_table.data_ptr(), tokens_before.data_ptr(), S, n, Hq, Hkv, D, P, num_pages,
         page_table.shape[1], max_tokens, int(mode), 0 if window is None else int(window),
         float(scale), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-        out.data_ptr(), _stream())
+        out.data_ptr(), _flag_ptr(err_flag), _stream())
     check("sfa_decode_step_paged", st)
     return out

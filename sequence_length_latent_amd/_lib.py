@@ -37,12 +37,12 @@ SIGNATURES = {
                                       _i32, _i32, _i32, _f32, _i64, _vp, _sz, _vp]),
     "sfa_decode_workspace_size": (_sz, [_i64, _i32, _i32, _i32, _i32, _i64]),
     "sfa_decode_step": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
-                                  _i64, _i64, _i32, _f32, _vp, _sz, _vp, _vp]),
+                                  _i64, _i64, _i32, _f32, _vp, _sz, _vp, _vp, _vp]),
     "sfa_decode_step_paged": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
                                         _i32, _i32, _i64, _i32, _i64, _i32, _i64, _f32, _vp, _sz,
-                                        _vp, _vp]),
+                                        _vp, _vp, _vp]),
     "sfa_decode_step_window": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
-                                         _i32, _i64, _i64, _i64, _f32, _vp, _sz, _vp, _vp]),
+                                         _i32, _i64, _i64, _i64, _f32, _vp, _sz, _vp, _vp, _vp]),
 }
 
 STATUS = {0: "HD_OK", 1: "HD_ERR_NULL", 2: "HD_ERR_SHAPE", 3: "HD_ERR_UNSUPPORTED",

@@ -66,14 +66,22 @@ struct DecodeArgs {
     uint32_t pshift, mpps, num_pages;
     uint16_t* out;             // [S, n, Hq, D]: written here when direct
     uint32_t direct;           // one split per view: the merged row is the output
+    int32_t* err;              // NULL or the caller's flag: set to 1 on an out-of-range page id
 };
 
+// true when a page id lies outside the pool (it is then clamped into it)
+__device__ __forceinline__ bool page_out_of_range(int32_t pg, uint32_t num_pages) {
+    return pg < 0 || pg >= (int32_t)num_pages;
+}
+
 // pool row of entry e of sequence seq (page ids outside the pool are clamped
-// into it, so no access leaves the pool)
+// into it, so no access leaves the pool; `bad` is set for such an id)
 __device__ __forceinline__ uint64_t paged_row(const int32_t* __restrict__ pt, uint32_t seq, uint32_t e,
-                                              uint32_t pshift, uint32_t mpps, uint32_t num_pages) {
+                                              uint32_t pshift, uint32_t mpps, uint32_t num_pages,
+                                              bool& bad) {
     const uint32_t slot = min(e >> pshift, mpps - 1u);
     int32_t pg = pt[(uint64_t)seq * mpps + slot];
+    bad = bad || page_out_of_range(pg, num_pages);
     pg = pg < 0 ? 0 : (pg >= (int32_t)num_pages ? (int32_t)num_pages - 1 : pg);
     return ((uint64_t)(uint32_t)pg << pshift) | (e & ((1u << pshift) - 1u));
 }
@@ -98,20 +106,25 @@ decode_append_kernel(const u32x4* __restrict__ k_new, const u32x4* __restrict__ 
                      const int32_t* __restrict__ tokens_before, uint32_t S, uint32_t n,
                      uint32_t row_chunks /* Hkv*D/8 */, uint64_t cache_seq_chunks,
                      uint32_t max_tokens, const int32_t* __restrict__ pt, uint32_t pshift,
-                     uint32_t mpps, uint32_t num_pages) {
+                     uint32_t mpps, uint32_t num_pages, int32_t* __restrict__ err) {
     const uint32_t idx = blockIdx.x * 256 + threadIdx.x;
     const uint32_t per_seq = n * row_chunks;
     if (idx >= S * per_seq) return;
     const uint32_t seq = idx / per_seq;
     const uint32_t rem = idx - seq * per_seq;      // s*row_chunks + w
-    const uint32_t T = clamp_tokens(tokens_before[seq], max_tokens);
+    const int32_t raw = tokens_before[seq];
+    const uint32_t T = clamp_tokens(raw, max_tokens);
+    // every kernel of the step clamps tokens_before the same way; this one,
+    // which reads every sequence's count, reports a count outside [0, max_tokens]
+    bool bad = raw < 0 || (uint32_t)raw > max_tokens;
     uint64_t dst;
     if constexpr (PAGED) {
         const uint32_t s = rem / row_chunks;
-        dst = paged_row(pt, seq, T * n + s, pshift, mpps, num_pages) * row_chunks + (rem - s * row_chunks);
+        dst = paged_row(pt, seq, T * n + s, pshift, mpps, num_pages, bad) * row_chunks + (rem - s * row_chunks);
     } else {
         dst = seq * cache_seq_chunks + (uint64_t)T * n * row_chunks + rem;
     }
+    if (bad && err != nullptr) *err = 1;
     kc[dst] = k_new[idx];
     vc[dst] = v_new[idx];
 }
@@ -271,7 +284,10 @@ decode_attend_kernel(const DecodeArgs a) {
     };
     auto store_tile = [&](const TileRegs& r, int slot) {
         if constexpr (PAGED) {
-            if (tid < DT) row_tab[slot * DT + tid] = pool_row(r.pg, r.pg_lo);
+            if (tid < DT) {
+                if (page_out_of_range(r.pg, a.num_pages) && a.err != nullptr) *a.err = 1;
+                row_tab[slot * DT + tid] = pool_row(r.pg, r.pg_lo);
+            }
         }
 #pragma unroll
         for (int i = 0; i < K_CHUNKS; ++i) {
@@ -379,6 +395,9 @@ decode_attend_kernel(const DecodeArgs a) {
             uint32_t lo0, lo1;
             fetch_page(0, tid, pg0, lo0);
             fetch_page(1, tid, pg1, lo1);
+            if ((page_out_of_range(pg0, a.num_pages) || page_out_of_range(pg1, a.num_pages)) &&
+                a.err != nullptr)
+                *a.err = 1;
             row_tab[tid] = pool_row(pg0, lo0);
             row_tab[DT + tid] = pool_row(pg1, lo1);
         }
@@ -550,8 +569,8 @@ hd_status decode_step(const uint16_t* q_new, const uint16_t* k_new, const uint16
                       uint16_t* k_cache, uint16_t* v_cache, const int32_t* tokens_before,
                       int64_t S, int32_t n, int32_t Hq, int32_t Hkv, int32_t D, int64_t C_max,
                       int64_t max_tokens, int32_t mode, float softmax_scale, void* workspace,
-                      size_t workspace_bytes, uint16_t* out, hipStream_t stream, int64_t window,
-                      const Paging& pg = Paging{}) {
+                      size_t workspace_bytes, uint16_t* out, int32_t* err_flag,
+                      hipStream_t stream, int64_t window, const Paging& pg = Paging{}) {
     const bool paged = pg.page_table != nullptr;
     if (S < 0 || n < 1 || Hq < 1 || Hkv < 1 || max_tokens < 0 || C_max < 0) return HD_ERR_SHAPE;
     if (!scale_ok(softmax_scale)) return HD_ERR_SHAPE;
@@ -585,7 +604,7 @@ hd_status decode_step(const uint16_t* q_new, const uint16_t* k_new, const uint16
             reinterpret_cast<const u32x4*>(k_new), reinterpret_cast<const u32x4*>(v_new),
             reinterpret_cast<u32x4*>(k_cache), reinterpret_cast<u32x4*>(v_cache),
             tokens_before, (uint32_t)S, (uint32_t)n, row_chunks, cache_seq / 8,
-            (uint32_t)max_tokens, pg.page_table, pg.pshift, pg.mpps, pg.num_pages);
+            (uint32_t)max_tokens, pg.page_table, pg.pshift, pg.mpps, pg.num_pages, err_flag);
         const hd_status st = launch_status();
         if (st != HD_OK) return st;
     }
@@ -622,6 +641,7 @@ hd_status decode_step(const uint16_t* q_new, const uint16_t* k_new, const uint16
     a.num_pages = pg.num_pages;
     a.out = out;
     a.direct = plan.nsplit == 1 ? 1u : 0u;
+    a.err = err_flag;
     const uint32_t rows = within ? G : R;
     const dim3 grid(plan.nsplit, (uint32_t)Hkv * (within ? (uint32_t)n : 1u), (uint32_t)S);
     if (D == 128) {
@@ -663,10 +683,10 @@ extern "C" hd_status sfa_decode_step(const uint16_t* q_new, const uint16_t* k_ne
                                      int32_t D, int64_t C_max, int64_t max_tokens,
                                      int32_t mode, float softmax_scale, void* workspace,
                                      size_t workspace_bytes, uint16_t* out,
-                                     hipStream_t stream) {
+                                     int32_t* err_flag, hipStream_t stream) {
     return hdsfa::decode_step(q_new, k_new, v_new, k_cache, v_cache, tokens_before, S, n, Hq, Hkv, D,
                               C_max, max_tokens, mode, softmax_scale, workspace, workspace_bytes, out,
-                              stream, 0);
+                              err_flag, stream, 0);
 }
 
 extern "C" hd_status sfa_decode_step_paged(const uint16_t* q_new, const uint16_t* k_new,
@@ -678,7 +698,7 @@ extern "C" hd_status sfa_decode_step_paged(const uint16_t* q_new, const uint16_t
                                            int64_t max_tokens, int32_t mode, int64_t window,
                                            float softmax_scale, void* workspace,
                                            size_t workspace_bytes, uint16_t* out,
-                                           hipStream_t stream) {
+                                           int32_t* err_flag, hipStream_t stream) {
     using namespace hdsfa;
     if (page_size < 1 || (page_size & (page_size - 1)) != 0) return HD_ERR_SHAPE;
     if (num_pages < 1 || num_pages > 0x7fffffffLL || max_pages_per_seq < 1) return HD_ERR_SHAPE;
@@ -695,7 +715,7 @@ extern "C" hd_status sfa_decode_step_paged(const uint16_t* q_new, const uint16_t
     if (S == 0) pg.page_table = nullptr;
     return decode_step(q_new, k_new, v_new, k_pages, v_pages, tokens_before, S, n, Hq, Hkv, D,
                        capacity, max_tokens, mode, softmax_scale, workspace, workspace_bytes, out,
-                       stream, window, pg);
+                       err_flag, stream, window, pg);
 }
 
 extern "C" hd_status sfa_decode_step_window(const uint16_t* q_new, const uint16_t* k_new,
@@ -705,9 +725,9 @@ extern "C" hd_status sfa_decode_step_window(const uint16_t* q_new, const uint16_
                                             int32_t D, int64_t C_max, int64_t max_tokens,
                                             int64_t window, float softmax_scale, void* workspace,
                                             size_t workspace_bytes, uint16_t* out,
-                                            hipStream_t stream) {
+                                            int32_t* err_flag, hipStream_t stream) {
     if (window < 1 || window > 0x7fffffffLL) return HD_ERR_SHAPE;
     return hdsfa::decode_step(q_new, k_new, v_new, k_cache, v_cache, tokens_before, S, n, Hq, Hkv, D,
                               C_max, max_tokens, 1, softmax_scale, workspace, workspace_bytes, out,
-                              stream, window);
+                              err_flag, stream, window);
 }

@@ -14,4 +14,4 @@ extern "C" const char* hd_status_string(int status) {
     }
 }
 
-extern "C" int hd_abi_version(void) { return 1; }
+extern "C" int hd_abi_version(void) { return 2; }

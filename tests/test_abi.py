@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    assert lib.hd_abi_version() == 1
+    assert lib.hd_abi_version() == 2
     seen = set()
     for code in range(7):
         s = lib.hd_status_string(code).decode()
@@ -158,7 +158,7 @@ def test_decode_validation(lib):
         wsb = kw.get("wsb", 1 << 30)
         return lib.sfa_decode_step(kw.get("q", FAKE), FAKE, FAKE, FAKE, FAKE, FAKE, a["S"], a["n"],
                                    a["Hq"], a["Hkv"], a["D"], a["C"], a["maxT"], a["mode"], 0.1,
-                                   ws, wsb, FAKE, None)
+                                   ws, wsb, FAKE, None, None)
 
     assert call(q=None) == NULL
     assert call(C=4 * 11 - 1) == CAP
@@ -173,7 +173,7 @@ def test_decode_validation(lib):
 def test_decode_window_validation(lib):
     def call(window, C=4 * 11, ws=FAKE, wsb=1 << 30, q=FAKE, S=2):
         return lib.sfa_decode_step_window(q, FAKE, FAKE, FAKE, FAKE, FAKE, S, 4, 8, 2, 128, C, 10,
-                                          window, 0.1, ws, wsb, FAKE, None)
+                                          window, 0.1, ws, wsb, FAKE, None, None)
 
     assert call(0) == SHAPE
     assert call(-3) == SHAPE
@@ -186,7 +186,8 @@ def test_decode_window_validation(lib):
 def test_decode_paged_validation(lib):
     def call(P=16, num_pages=64, mpps=8, mode=1, window=0, C=None, pt=FAKE, q=FAKE, S=2, wsb=1 << 30):
         return lib.sfa_decode_step_paged(q, FAKE, FAKE, FAKE, FAKE, pt, FAKE, S, 4, 8, 2, 128, P,
-                                         num_pages, mpps, 10, mode, window, 0.1, FAKE, wsb, FAKE, None)
+                                         num_pages, mpps, 10, mode, window, 0.1, FAKE, wsb, FAKE, None,
+                                         None)
 
     assert call(P=12) == SHAPE                  # not a power of two
     assert call(P=0) == SHAPE
@@ -278,8 +279,8 @@ def test_softmax_scale_must_be_finite_and_positive(lib):
         assert lib.sfa_attn_bwd(*args8, 1, 2, 8, 4, 2, 128, sc, 1, FAKE, 1 << 20, None) == SHAPE
         assert lib.sfa_attn_bwd_window(*args8, 1, 2, 8, 4, 2, 128, sc, 4, FAKE, 1 << 20, None) == SHAPE
         assert lib.sfa_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 8, 2, 128, 44, 10, 1, sc,
-                                   FAKE, 1 << 30, FAKE, None) == SHAPE
+                                   FAKE, 1 << 30, FAKE, None, None) == SHAPE
         assert lib.sfa_decode_step_window(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 8, 2, 128, 44, 10, 8, sc,
-                                          FAKE, 1 << 30, FAKE, None) == SHAPE
+                                          FAKE, 1 << 30, FAKE, None, None) == SHAPE
         assert lib.sfa_decode_step_paged(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 8, 2, 128, 16, 64, 8,
-                                         10, 1, 0, sc, FAKE, 1 << 30, FAKE, None) == SHAPE
+                                         10, 1, 0, sc, FAKE, 1 << 30, FAKE, None, None) == SHAPE

@@ -823,6 +823,70 @@ def test_decode_paged_other_shapes(n, Hq, Hkv, D, mode, P):
     assert torch.equal(ref.view(torch.int16), got.view(torch.int16))
 
 
+@pytest.mark.parametrize("mode", [WITHIN, MIX])
+def test_decode_error_flag_token_counts(mode):
+    """A tokens_before value outside [0, max_tokens] is clamped into it on the
+    device (every access stays in the cache) and raises the caller's flag; the
+    step is then the step with the clamped counts, bit for bit.  In-range
+    counts leave the flag at zero."""
+    cfg = si.DECODE
+    S, T = 3, 100
+    qn, kn, vn, kc, vc, _ = si.decode_inputs(cfg, device=DEV, S=S, T=T)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    good = torch.tensor([100, 0, 40], dtype=torch.int32, device=DEV)
+    kc1, vc1 = kc.clone(), vc.clone()
+    ref = hd.decode_step(qn, kn, vn, kc1, vc1, good, cfg.n, T, mode, cfg.scale, err_flag=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+    bad = torch.tensor([130, -4, 40], dtype=torch.int32, device=DEV)
+    kc2, vc2 = kc.clone(), vc.clone()
+    got = hd.decode_step(qn, kn, vn, kc2, vc2, bad, cfg.n, T, mode, cfg.scale, err_flag=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 1
+    assert torch.equal(ref.view(torch.int16), got.view(torch.int16))
+    assert torch.equal(kc1.view(torch.int16), kc2.view(torch.int16))
+    assert torch.equal(vc1.view(torch.int16), vc2.view(torch.int16))
+
+
+@pytest.mark.parametrize("mode", [WITHIN, MIX])
+def test_decode_paged_error_flag_page_ids(mode):
+    """A page id outside the pool, on a page the step reads, is clamped into
+    the pool (-1 -> page 0, num_pages + 5 -> the last page) and raises the
+    flag; the result equals the step over a table holding the clamped ids.
+    Garbage in table slots past a sequence's live entries is never read and
+    leaves the flag at zero."""
+    cfg = si.DECODE
+    S, T, P = 3, 100, 16
+    tb = [100, 20, 55]
+    qn, kn, vn, kc, vc, tbt = si.decode_inputs(cfg, device=DEV, S=S, T=T, tokens_before=tb)
+    kp, vp, pt = _paged_from(kc, vc, P, 7300 + mode)
+    num_pages = kp.shape[0]
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    # sequence 1 holds (20 + 1) * 4 = 84 entries: pages 0..5; slots 6.. are unused
+    pt_unused = pt.clone()
+    pt_unused[1, 7:] = -7
+    out0 = hd.decode_step_paged(qn, kn, vn, kp.clone(), vp.clone(), pt_unused, tbt, cfg.n, T, mode,
+                                cfg.scale, err_flag=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+    bad = pt.clone()
+    bad[0, 3] = -1
+    bad[2, 1] = num_pages + 5
+    clamped = pt.clone()
+    clamped[0, 3] = 0
+    clamped[2, 1] = num_pages - 1
+    ref = hd.decode_step_paged(qn, kn, vn, kp.clone(), vp.clone(), clamped, tbt, cfg.n, T, mode,
+                               cfg.scale)
+    got = hd.decode_step_paged(qn, kn, vn, kp.clone(), vp.clone(), bad, tbt, cfg.n, T, mode,
+                               cfg.scale, err_flag=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 1
+    assert torch.equal(ref.view(torch.int16), got.view(torch.int16))
+    assert torch.equal(out0.view(torch.int16),
+                       hd.decode_step_paged(qn, kn, vn, kp.clone(), vp.clone(), pt, tbt, cfg.n, T,
+                                            mode, cfg.scale).view(torch.int16))
+
+
 def test_decode_paged_oracle_on_gathered_pages():
     """Paged decode against the oracle on the rows gathered back through the
     page table (page size 32, mixing with a window)."""
