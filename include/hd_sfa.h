@@ -52,7 +52,9 @@ typedef enum hd_status {
                                 library's 32-bit index range                     */
     HD_ERR_CAPACITY = 4,     /* KV cache too small for the appended entries      */
     HD_ERR_LAUNCH = 5,       /* the HIP runtime refused a launch                 */
-    HD_ERR_WORKSPACE = 6     /* decode workspace NULL or smaller than required   */
+    HD_ERR_WORKSPACE = 6,    /* decode workspace NULL or smaller than required   */
+    HD_ERR_SCRATCH = 7       /* the call needs more than the library's static
+                                scratch (sfa_decode_step_noalloc) holds          */
 } hd_status;
 
 /* Static, NUL-terminated description of a status code; never NULL. */
@@ -317,6 +319,35 @@ hd_status sfa_decode_step(const uint16_t* q_new, const uint16_t* k_new,
                           int32_t mode, float softmax_scale, void* workspace,
                           size_t workspace_bytes, uint16_t* out, int32_t* err_flag,
                           hipStream_t stream);
+
+/*
+ * sfa_decode_step_noalloc -- sfa_decode_step for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Same arguments (without
+ * workspace and workspace_bytes), results bit for bit those of
+ * sfa_decode_step, same errors, plus:
+ *
+ *   - the split partials live in a static array of 16 MiB per device, part
+ *     of the library's code object (held by every GPU the library runs on
+ *     until the process ends).  Its device address is looked up once per
+ *     device, on the first call there.  The call itself allocates nothing.
+ *   - a call whose partials need more than 16 MiB returns HD_ERR_SCRATCH and
+ *     launches nothing.  Partials take S*Hkv*(n*Hq/Hkv)*splits*(D+2)*4 bytes
+ *     when a view is split (a view is split only while there are fewer than
+ *     512 (sequence, KV head) views), none otherwise.  Use sfa_decode_step
+ *     with a workspace for such sizes.
+ *   - every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (different streams, or host threads) race and must be
+ *     serialised by the caller.  Nothing in the array needs to start at
+ *     zero: each call writes every partial it reads.
+ */
+hd_status sfa_decode_step_noalloc(const uint16_t* q_new, const uint16_t* k_new,
+                                  const uint16_t* v_new, uint16_t* k_cache,
+                                  uint16_t* v_cache, const int32_t* tokens_before,
+                                  int64_t S, int32_t n, int32_t Hq, int32_t Hkv,
+                                  int32_t D, int64_t C_max, int64_t max_tokens,
+                                  int32_t mode, float softmax_scale, uint16_t* out,
+                                  int32_t* err_flag, hipStream_t stream);
 
 /*
  * sfa_decode_step_paged -- sfa_decode_step over a paged cache (the retained

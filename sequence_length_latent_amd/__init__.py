@@ -17,7 +17,7 @@ from ._lib import HDError, check, load  # noqa: F401
 
 __all__ = ["expand", "final_stream_rows", "cyclic_replicate", "stream_attn", "mix_attn",
            "mix_attn_window", "attn_fwd", "attn_bwd", "decode_workspace_size", "decode_step",
-           "decode_step_paged",
+           "decode_step_noalloc", "decode_step_paged",
            "HDError", "load", "WITHIN", "MIX"]
 
 WITHIN = 0
@@ -266,6 +266,41 @@ def decode_step(q_new, k_new, v_new, k_cache, v_cache, tokens_before, n: int,
                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                 out.data_ptr(), _flag_ptr(err_flag), _stream())
     check("sfa_decode_step", st)
+    return out
+
+
+def decode_step_noalloc(q_new, k_new, v_new, k_cache, v_cache, tokens_before, n: int,
+                        max_tokens: int, mode: int, scale: float, out=None, err_flag=None):
+    """decode_step without a workspace (sfa_decode_step_noalloc): the split
+    partials live in the library's static 16 MiB per-device scratch, so the
+    call allocates nothing given ``out``.  Bitwise the same results as
+    decode_step; calls that overlap in time on one GPU race on the scratch."""
+    for t, nm in ((q_new, "q_new"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"),
+                  (v_cache, "v_cache")):
+        _need(t, nm, torch.bfloat16, 4)
+    _need(tokens_before, "tokens_before", torch.int32, 1)
+    S, n_, Hq, D = q_new.shape
+    if n_ != n:
+        raise ValueError("q_new must be [S, n, Hq, D]")
+    Hkv = k_new.shape[2]
+    C = k_cache.shape[1]
+    if tuple(k_new.shape) != (S, n, Hkv, D) or tuple(v_new.shape) != (S, n, Hkv, D):
+        raise ValueError("k_new/v_new must be [S, n, Hkv, D]")
+    if tuple(k_cache.shape) != (S, C, Hkv, D) or tuple(v_cache.shape) != (S, C, Hkv, D):
+        raise ValueError("caches must be [S, C, Hkv, D]")
+    if tuple(tokens_before.shape) != (S,):
+        raise ValueError("tokens_before must be [S]")
+    if out is None:
+        out = torch.empty_like(q_new)
+    _need(out, "out", torch.bfloat16, 4)
+    if out.shape != q_new.shape:
+        raise ValueError("out must match q_new")
+    st = load().sfa_decode_step_noalloc(q_new.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                                        k_cache.data_ptr(), v_cache.data_ptr(),
+                                        tokens_before.data_ptr(), S, n, Hq, Hkv, D, C, max_tokens,
+                                        int(mode), float(scale), out.data_ptr(),
+                                        _flag_ptr(err_flag), _stream())
+    check("sfa_decode_step_noalloc", st)
     return out
 
 

@@ -38,6 +38,8 @@ SIGNATURES = {
     "sfa_decode_workspace_size": (_sz, [_i64, _i32, _i32, _i32, _i32, _i64]),
     "sfa_decode_step": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
                                   _i64, _i64, _i32, _f32, _vp, _sz, _vp, _vp, _vp]),
+    "sfa_decode_step_noalloc": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
+                                          _i32, _i64, _i64, _i32, _f32, _vp, _vp, _vp]),
     "sfa_decode_step_paged": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
                                         _i32, _i32, _i64, _i32, _i64, _i32, _i64, _f32, _vp, _sz,
                                         _vp, _vp, _vp]),
@@ -46,7 +48,7 @@ SIGNATURES = {
 }
 
 STATUS = {0: "HD_OK", 1: "HD_ERR_NULL", 2: "HD_ERR_SHAPE", 3: "HD_ERR_UNSUPPORTED",
-          4: "HD_ERR_CAPACITY", 5: "HD_ERR_LAUNCH", 6: "HD_ERR_WORKSPACE"}
+          4: "HD_ERR_CAPACITY", 5: "HD_ERR_LAUNCH", 6: "HD_ERR_WORKSPACE", 7: "HD_ERR_SCRATCH"}
 
 
 class HDError(RuntimeError):

@@ -1,6 +1,7 @@
 // Hidden Decoding decode step over the retained per-stream KV cache
 // (sfa_decode_workspace_size, sfa_decode_step, sfa_decode_step_window,
-// sfa_decode_step_paged).
+// sfa_decode_step_paged, and sfa_decode_step_noalloc, which keeps the split
+// partials in a static per-device array instead of a caller's workspace).
 //
 // "Hidden Decoding at Scale" review, sections Method and Limitations: the KV
 // of every stream is kept, so the cache holds n entries per token and later
@@ -33,6 +34,8 @@
 // same kernels look every cache row up through the table (PAGED instances).
 // No atomics: results are bitwise reproducible run to run.
 #include "common.h"
+
+#include <mutex>
 
 namespace hdsfa {
 
@@ -565,11 +568,45 @@ struct Paging {
     uint32_t pshift = 0, mpps = 0, num_pages = 0;
 };
 
+// Static scratch of sfa_decode_step_noalloc: the split partials of one call,
+// one array per device (each GPU the library runs on holds its own copy until
+// the process ends).  Host code never uses the array's name as an address:
+// its device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kNoallocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+hipError_t g_scratch_status[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+
+// device address of the current device's scratch array (nullptr on failure)
+void* scratch_on_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        g_scratch_status[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_status[dev] == hipSuccess ? p : nullptr;
+    });
+    return g_scratch_status[dev] == hipSuccess ? g_scratch_ptr[dev] : nullptr;
+}
+
+// Where the split partials go: the caller's workspace (checked against
+// sfa_decode_workspace_size, stride = the larger split count of the two
+// modes) or, with use_static, the static scratch (stride = this call's own
+// split count, nothing at all when every view is one split).
+struct PartialsBuf {
+    void* workspace = nullptr;
+    size_t workspace_bytes = 0;
+    bool use_static = false;
+};
+
 hd_status decode_step(const uint16_t* q_new, const uint16_t* k_new, const uint16_t* v_new,
                       uint16_t* k_cache, uint16_t* v_cache, const int32_t* tokens_before,
                       int64_t S, int32_t n, int32_t Hq, int32_t Hkv, int32_t D, int64_t C_max,
-                      int64_t max_tokens, int32_t mode, float softmax_scale, void* workspace,
-                      size_t workspace_bytes, uint16_t* out, int32_t* err_flag,
+                      int64_t max_tokens, int32_t mode, float softmax_scale, const PartialsBuf& pb,
+                      uint16_t* out, int32_t* err_flag,
                       hipStream_t stream, int64_t window, const Paging& pg = Paging{}) {
     const bool paged = pg.page_table != nullptr;
     if (S < 0 || n < 1 || Hq < 1 || Hkv < 1 || max_tokens < 0 || C_max < 0) return HD_ERR_SHAPE;
@@ -585,13 +622,31 @@ hd_status decode_step(const uint16_t* q_new, const uint16_t* k_new, const uint16
     if (!aligned16(q_new) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
         !aligned16(v_cache) || !aligned16(out))
         return HD_ERR_SHAPE;
-    const size_t need = sfa_decode_workspace_size(S, n, Hq, Hkv, D, max_tokens);
-    if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return HD_ERR_WORKSPACE;
-
     const bool within = mode == 0;
     const uint32_t G = (uint32_t)(Hq / Hkv);
     const uint32_t R = (uint32_t)n * G;
     const uint64_t cache_seq = (uint64_t)C_max * Hkv * D;
+
+    const SplitPlan plan = plan_splits((uint64_t)S, (uint32_t)n, (uint32_t)Hkv, (uint64_t)max_tokens, within,
+                                       within ? 0u : (uint64_t)window);
+    float* ws = nullptr;
+    uint32_t ws_nsplit = 1;
+    if (!pb.use_static) {
+        const size_t need = sfa_decode_workspace_size(S, n, Hq, Hkv, D, max_tokens);
+        if (pb.workspace == nullptr || pb.workspace_bytes < need || !aligned16(pb.workspace))
+            return HD_ERR_WORKSPACE;
+        // the workspace stride uses the larger plan of the two modes
+        const SplitPlan pw = plan_splits((uint64_t)S, (uint32_t)n, (uint32_t)Hkv, (uint64_t)max_tokens, true);
+        const SplitPlan pm = plan_splits((uint64_t)S, (uint32_t)n, (uint32_t)Hkv, (uint64_t)max_tokens, false);
+        ws_nsplit = pw.nsplit > pm.nsplit ? pw.nsplit : pm.nsplit;
+        ws = static_cast<float*>(pb.workspace);
+    } else if (plan.nsplit > 1) {
+        ws_nsplit = plan.nsplit;
+        const uint64_t need = (uint64_t)S * Hkv * R * ws_nsplit * (uint64_t)(D + 2) * sizeof(float);
+        if (need > kNoallocScratchBytes) return HD_ERR_SCRATCH;
+        ws = static_cast<float*>(scratch_on_current_device());
+        if (ws == nullptr) return HD_ERR_LAUNCH;
+    }
 
     // 1. append
     {
@@ -610,19 +665,12 @@ hd_status decode_step(const uint16_t* q_new, const uint16_t* k_new, const uint16
     }
 
     // 2. attend
-    const SplitPlan plan = plan_splits((uint64_t)S, (uint32_t)n, (uint32_t)Hkv, (uint64_t)max_tokens, within,
-                                       within ? 0u : (uint64_t)window);
-    // the workspace stride uses the larger plan of the two modes
-    const SplitPlan pw = plan_splits((uint64_t)S, (uint32_t)n, (uint32_t)Hkv, (uint64_t)max_tokens, true);
-    const SplitPlan pm = plan_splits((uint64_t)S, (uint32_t)n, (uint32_t)Hkv, (uint64_t)max_tokens, false);
-    const uint32_t ws_nsplit = pw.nsplit > pm.nsplit ? pw.nsplit : pm.nsplit;
-
     DecodeArgs a;
     a.q = q_new;
     a.kc = k_cache;
     a.vc = v_cache;
     a.tokens_before = tokens_before;
-    a.ws = static_cast<float*>(workspace);
+    a.ws = ws;
     a.cache_seq = cache_seq;
     a.n = (uint32_t)n;
     a.Hq = (uint32_t)Hq;
@@ -684,9 +732,24 @@ extern "C" hd_status sfa_decode_step(const uint16_t* q_new, const uint16_t* k_ne
                                      int32_t mode, float softmax_scale, void* workspace,
                                      size_t workspace_bytes, uint16_t* out,
                                      int32_t* err_flag, hipStream_t stream) {
+    hdsfa::PartialsBuf pb;
+    pb.workspace = workspace;
+    pb.workspace_bytes = workspace_bytes;
     return hdsfa::decode_step(q_new, k_new, v_new, k_cache, v_cache, tokens_before, S, n, Hq, Hkv, D,
-                              C_max, max_tokens, mode, softmax_scale, workspace, workspace_bytes, out,
-                              err_flag, stream, 0);
+                              C_max, max_tokens, mode, softmax_scale, pb, out, err_flag, stream, 0);
+}
+
+extern "C" hd_status sfa_decode_step_noalloc(const uint16_t* q_new, const uint16_t* k_new,
+                                             const uint16_t* v_new, uint16_t* k_cache,
+                                             uint16_t* v_cache, const int32_t* tokens_before,
+                                             int64_t S, int32_t n, int32_t Hq, int32_t Hkv,
+                                             int32_t D, int64_t C_max, int64_t max_tokens,
+                                             int32_t mode, float softmax_scale, uint16_t* out,
+                                             int32_t* err_flag, hipStream_t stream) {
+    hdsfa::PartialsBuf pb;
+    pb.use_static = true;
+    return hdsfa::decode_step(q_new, k_new, v_new, k_cache, v_cache, tokens_before, S, n, Hq, Hkv, D,
+                              C_max, max_tokens, mode, softmax_scale, pb, out, err_flag, stream, 0);
 }
 
 extern "C" hd_status sfa_decode_step_paged(const uint16_t* q_new, const uint16_t* k_new,
@@ -713,9 +776,11 @@ extern "C" hd_status sfa_decode_step_paged(const uint16_t* q_new, const uint16_t
     pg.num_pages = (uint32_t)num_pages;
     const int64_t capacity = (int64_t)max_pages_per_seq * page_size;   // entries a sequence can hold
     if (S == 0) pg.page_table = nullptr;
+    PartialsBuf pb;
+    pb.workspace = workspace;
+    pb.workspace_bytes = workspace_bytes;
     return decode_step(q_new, k_new, v_new, k_pages, v_pages, tokens_before, S, n, Hq, Hkv, D,
-                       capacity, max_tokens, mode, softmax_scale, workspace, workspace_bytes, out,
-                       err_flag, stream, window, pg);
+                       capacity, max_tokens, mode, softmax_scale, pb, out, err_flag, stream, window, pg);
 }
 
 extern "C" hd_status sfa_decode_step_window(const uint16_t* q_new, const uint16_t* k_new,
@@ -727,7 +792,9 @@ extern "C" hd_status sfa_decode_step_window(const uint16_t* q_new, const uint16_
                                             size_t workspace_bytes, uint16_t* out,
                                             int32_t* err_flag, hipStream_t stream) {
     if (window < 1 || window > 0x7fffffffLL) return HD_ERR_SHAPE;
+    hdsfa::PartialsBuf pb;
+    pb.workspace = workspace;
+    pb.workspace_bytes = workspace_bytes;
     return hdsfa::decode_step(q_new, k_new, v_new, k_cache, v_cache, tokens_before, S, n, Hq, Hkv, D,
-                              C_max, max_tokens, 1, softmax_scale, workspace, workspace_bytes, out,
-                              err_flag, stream, window);
+                              C_max, max_tokens, 1, softmax_scale, pb, out, err_flag, stream, window);
 }

@@ -10,6 +10,7 @@ extern "C" const char* hd_status_string(int status) {
         case HD_ERR_CAPACITY: return "KV cache capacity too small for the appended entries";
         case HD_ERR_LAUNCH: return "kernel launch failed";
         case HD_ERR_WORKSPACE: return "decode workspace missing, misaligned or too small";
+        case HD_ERR_SCRATCH: return "call needs more than the library's 16 MiB static decode scratch; pass a workspace to sfa_decode_step";
         default: return "unknown status";
     }
 }

@@ -13,7 +13,7 @@ from sequence_length_latent_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "hd_sfa.h")
 
-OK, NULL, SHAPE, UNSUP, CAP, LAUNCH, WS = range(7)
+OK, NULL, SHAPE, UNSUP, CAP, LAUNCH, WS, SCRATCH = range(8)
 
 
 def _declared():
@@ -35,7 +35,8 @@ def test_every_declared_symbol_is_exported(lib):
                           "sfa_attn_bwd_workspace_size", "sfa_attn_bwd",
                           "sfa_attn_fwd_window", "sfa_attn_bwd_window",
                           "sfa_decode_workspace_size", "sfa_decode_step",
-                          "sfa_decode_step_window", "sfa_decode_step_paged"}
+                          "sfa_decode_step_window", "sfa_decode_step_paged",
+                          "sfa_decode_step_noalloc"}
     for name in names:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, name
@@ -44,7 +45,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_status_strings(lib):
     assert lib.hd_abi_version() == 2
     seen = set()
-    for code in range(7):
+    for code in range(8):
         s = lib.hd_status_string(code).decode()
         assert s and s not in seen
         seen.add(s)
@@ -168,6 +169,27 @@ def test_decode_validation(lib):
     assert call(ws=None) == WS
     assert call(wsb=16) == WS
     assert call(S=0, q=None) == OK
+
+
+def test_decode_noalloc_validation(lib):
+    """The no-workspace decode validates like sfa_decode_step and rejects, on
+    the host and before any launch, a call whose split partials would not fit
+    its 16 MiB static scratch."""
+    def call(S=2, n=4, Hq=8, Hkv=2, D=128, C=4 * 11, maxT=10, mode=1, q=FAKE):
+        return lib.sfa_decode_step_noalloc(q, FAKE, FAKE, FAKE, FAKE, FAKE, S, n, Hq, Hkv, D, C, maxT,
+                                           mode, 0.1, FAKE, None, None)
+
+    assert call(q=None) == NULL
+    assert call(C=4 * 11 - 1) == CAP
+    assert call(mode=2) == SHAPE
+    assert call(Hkv=3) == SHAPE
+    assert call(D=80) == UNSUP
+    assert call(S=0, q=None) == OK
+    # 16 sequences x 8 KV heads (128 views, 4 splits each) x 64 query rows x
+    # 130 floats: 17.0 MB of partials > 16 MiB
+    big = dict(S=16, n=8, Hq=64, Hkv=8, D=128, maxT=4095, C=8 * 4096)
+    assert call(**big) == SCRATCH
+    assert lib.hd_status_string(SCRATCH).decode().startswith("call needs more")
 
 
 def test_decode_window_validation(lib):
