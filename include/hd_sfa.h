@@ -135,6 +135,10 @@ hd_status hd_cyclic_replicate(const uint16_t* tables, int32_t n_old, int64_t V, 
  * contractions run on bf16 matrix cores; out is rounded to nearest even.
  * Work skipped: only token tiles of the query's own stream that are not in
  * its future are visited, so the cost grows linearly in n.
+ * The prefill entry points run a persistent grid of one workgroup per compute
+ * unit; the environment variable HD_SFA_PREFILL_WORKGROUPS (a count from 1 to
+ * 65536, read at every call) sets another grid size, a testing and tuning
+ * control that never changes a result bit.
  */
 hd_status sfa_stream_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                           uint16_t* out, int64_t B, int32_t n, int64_t L,

@@ -172,15 +172,16 @@ def _softmax_rows(scores):
     return p / p.sum(axis=1, keepdims=True)
 
 
-def attention_rows(q_rows, q_pos, k, v, n, mode, scale, window=None):
+def attention_rows(q_rows, q_pos, k, v, n, mode, scale, window=None, k_pos=None):
     """softmax(scale * q k^T + mask) v for some query rows of one head.
 
     q_rows : float64 [R, D]   the queries
     q_pos  : int [R]          their positions in the expanded sequence
-    k, v   : float64 [Nk, D]  keys/values at positions 0..Nk-1
+    k, v   : float64 [Nk, D]  keys/values
+    k_pos  : int [Nk]         their positions (default 0..Nk-1)
     returns (out [R, D], probs [R, Nk]) in float64.
     """
-    j = np.arange(k.shape[0])[None, :]
+    j = (np.arange(k.shape[0]) if k_pos is None else np.asarray(k_pos))[None, :]
     mask = visible(np.asarray(q_pos)[:, None], j, n, mode, window)
     scores = scale * (q_rows @ k.T)
     scores = np.where(mask, scores, -np.inf)
@@ -202,7 +203,10 @@ def prefill_ref(q, k, v, n, mode, scale, rows=None, heads=None, batches=None,
 
     Query head h reads KV head h // (Hq // Hkv) (reading R6).  Rows are handled
     ``chunk`` at a time only to bound memory; each row's arithmetic is the
-    definition above, independent of the others.
+    definition above, independent of the others.  Within-stream rows are taken
+    one stream at a time and given only that stream's keys: the visibility
+    rule removes every other key, so leaving them out changes no value (it
+    only spares the work of scores that the mask discards).
     """
     q = np.asarray(q)
     k = np.asarray(k)
@@ -221,13 +225,18 @@ def prefill_ref(q, k, v, n, mode, scale, rows=None, heads=None, batches=None,
             g = h // G
             kf = bf16_bits_to_f64(k[b, :, g, :])
             vf = bf16_bits_to_f64(v[b, :, g, :])
-            for c0 in range(0, len(rows), chunk):
-                r = rows[c0:c0 + chunk]
-                # keys later than the last requested row are never visible
-                nk = int(r.max()) + 1
-                qf = bf16_bits_to_f64(q[b, r, h, :])
-                o, _ = attention_rows(qf, r, kf[:nk], vf[:nk], n, mode, scale, window)
-                out[bi, c0:c0 + len(r), hi, :] = o
+            groups = [np.arange(len(rows))] if mode != WITHIN else \
+                [np.nonzero(rows % n == s)[0] for s in range(n)]
+            for sel in groups:
+                for c0 in range(0, len(sel), chunk):
+                    idx = sel[c0:c0 + chunk]
+                    r = rows[idx]
+                    # keys later than the last requested row are never visible
+                    nk = int(r.max()) + 1
+                    kp = np.arange(nk) if mode != WITHIN else np.arange(int(r[0]) % n, nk, n)
+                    qf = bf16_bits_to_f64(q[b, r, h, :])
+                    o, _ = attention_rows(qf, r, kf[kp], vf[kp], n, mode, scale, window, k_pos=kp)
+                    out[bi, idx, hi, :] = o
     return out
 
 

@@ -25,8 +25,9 @@
 //
 // Work items are (query tile, batch, view, KV head, head pack), listed longest
 // causal extent first.  The grid is persistent, one workgroup per compute
-// unit: workgroup b takes item r*grid + b on even rounds r and
-// r*grid + (grid-1-b) on odd rounds, which evens out the triangular costs.
+// unit (HD_SFA_PREFILL_WORKGROUPS in the environment sets another count):
+// workgroup b takes item r*grid + b on even rounds r and r*grid + (grid-1-b)
+// on odd rounds, which evens out the triangular costs.
 // While a workgroup normalises and stores one item's output, the Q fragments
 // and first K/V tiles of its next item are already on their way.
 //
@@ -53,6 +54,7 @@
 #include "common.h"
 #include "prefill_asm.h"
 
+#include <cstdlib>
 #include <type_traits>
 
 namespace hdsfa {
@@ -610,6 +612,20 @@ int device_cus() {
     return c;
 }
 
+// Workgroups of the persistent grid: one per compute unit, unless the
+// environment variable HD_SFA_PREFILL_WORKGROUPS holds a count from 1 to
+// 65536 (a testing and tuning control).  Every work item is computed the same
+// way whichever workgroup takes it, so the count never changes a result.
+uint64_t persistent_workgroups() {
+    uint64_t g = (uint64_t)device_cus();
+    if (const char* e = std::getenv("HD_SFA_PREFILL_WORKGROUPS")) {
+        char* end = nullptr;
+        const long v = std::strtol(e, &end, 10);
+        if (end != e && *end == '\0' && v >= 1 && v <= 65536) g = (uint64_t)v;
+    }
+    return g;
+}
+
 hd_status launch_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          uint16_t* out, int64_t B, int32_t n, int64_t L, int32_t Hq,
                          int32_t Hkv, int32_t D, float scale, hipStream_t stream,
@@ -654,7 +670,8 @@ hd_status launch_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v
     const uint64_t items = (uint64_t)a.n_qtiles * a.B * a.groups * a.Hkv * a.n_hpacks;
     if (items > 0x7fffffffULL) return HD_ERR_UNSUPPORTED;
     a.n_items = (uint32_t)items;
-    const uint64_t blocks = items < (uint64_t)device_cus() ? items : (uint64_t)device_cus();
+    const uint64_t wgs = persistent_workgroups();
+    const uint64_t blocks = items < wgs ? items : wgs;
     // a window at least as long as the view masks nothing: the causal kernel
     const bool win = window > 0 && window < (int64_t)a.len;
     a.window = win ? (uint32_t)window : 0u;

@@ -1,17 +1,37 @@
 """Shared comparison helpers for the GPU parity tests.
 
-Floating-point bar (reading of "max-abs 1e-2 / max-rel 2e-2", bf16 in/out,
-fp32 accumulate): an output passes when, for every element,
+The floating-point bar "max-abs 1e-2 / max-rel 2e-2" (bf16 in and out, fp32
+accumulate) is checked in two parts.
+
+Base bar (every test): for every element
     |gpu - ref| <= 1e-2 + 2e-2 * |ref|
-and, over the whole tensor,
+and, over the whole tensor (norm-relative),
     max |gpu - ref| <= 2e-2 * max |ref|.
-The second (norm-relative) term keeps the bar discriminating when outputs are
-small; the negative controls in the tests must fail it.
+The norm-relative term keeps the bar discriminating when outputs are small;
+the negative controls in the tests must fail it.
+
+Max-abs part (forward outputs, ``c10=True``): every element within
+    1e-2                                   (``ref_abs`` not given), or
+    max(1e-2, halfulp(ref) + 2^-8 * ref_abs)   (``ref_abs`` given).
+The first is the stated max-abs 1e-2 itself; the forward tests on the
+workloads' own input distributions use it.  The second is for stress inputs
+(peaked softmax, unscaled queries, one-hot or prefix-mean pins) whose outputs
+reach magnitudes where the two bf16 roundings the stated precision makes can
+exceed 1e-2 on a correct result: the probabilities enter the value product
+as bf16 (relative error up to 2^-8 each, so up to 2^-8 * sum_j p_j |v_j|),
+and the output is stored as bf16 (up to half an ulp of the result).
+``ref_abs`` is sum_j p_j |v_j|, the oracle's output for the same call with
+|V| in place of V.
 """
 import numpy as np
 
 ATOL = 1e-2
 RTOL = 2e-2
+BF16_UNIT_ROUNDOFF = 2.0 ** -8
+
+# (what, max abs error, max |ref|, worst error / max-abs allowance) of every
+# checked tensor, for the margin report written at the end of a session
+RECORD = []
 
 
 def close_report(got, ref):
@@ -24,8 +44,40 @@ def close_report(got, ref):
     return elem_ok and norm_ok, float(err.max()) if ref.size else 0.0
 
 
-def assert_close(got, ref, what=""):
+def half_ulp_bf16(x):
+    """Half the spacing of bf16 values at |x| (8 significant bits): the
+    largest error of rounding a real of that binade to bf16."""
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    _, e = np.frexp(x)                  # x = m * 2^e, 0.5 <= m < 1
+    return np.where(x > 0, np.ldexp(1.0, e - 9), 0.0)
+
+
+def maxabs_report(got, ref, ref_abs=None):
+    """(ok, worst error / allowance) of the max-abs part."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if not ref.size:
+        return True, 0.0
+    if ref_abs is None:
+        allow = ATOL
+    else:
+        allow = np.maximum(ATOL, half_ulp_bf16(ref) + BF16_UNIT_ROUNDOFF * np.asarray(ref_abs))
+    ratio = float((np.abs(got - ref) / allow).max())
+    return ratio <= 1.0, ratio
+
+
+def assert_close(got, ref, what="", c10=True, ref_abs=None):
     ok, e = close_report(got, ref)
     ref = np.asarray(ref)
-    assert ok, f"{what}: max abs err {e:.3e} (ref max {np.abs(ref).max():.3e})"
+    scale = float(np.abs(ref).max()) if ref.size else 0.0
+    ok2, ratio = maxabs_report(got, ref, ref_abs)
+    RECORD.append((what + ("" if ref_abs is None else " [rounding-aware]"), e, scale, ratio))
+    assert ok, f"{what}: max abs err {e:.3e} (ref max {scale:.3e})"
+    if c10:
+        assert ok2, f"{what}: max-abs part violated, worst error/allowance {ratio:.3f} (ref max {scale:.3e})"
     return e
+
+
+def abs_bits(bits):
+    """bf16 bit patterns of |x| (sign bit cleared)."""
+    return np.asarray(bits, dtype=np.uint16) & np.uint16(0x7FFF)

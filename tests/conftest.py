@@ -28,3 +28,17 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """With HD_SFA_MARGINS_OUT set, write every checked tensor's worst error
+    against the floating-point bar (tests/_check.RECORD) to that JSON file."""
+    path = os.environ.get("HD_SFA_MARGINS_OUT")
+    if not path:
+        return
+    import json
+    from tests import _check
+    rows = [{"what": w, "max_abs_err": e, "max_abs_ref": r, "worst_err_over_maxabs_allowance": q}
+            for (w, e, r, q) in _check.RECORD]
+    with open(path, "w") as f:
+        json.dump(rows, f, indent=1)

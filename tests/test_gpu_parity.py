@@ -14,6 +14,7 @@ import oracle
 import sequence_length_latent_amd as hd
 import sfa_inputs as si
 from tests._check import assert_close, close_report
+from tests._refs import decode_pair, prefill_pair
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -155,8 +156,8 @@ def test_prefill_tiny_all_rows(mode):
     cfg = si.TINY
     q, k, v = si.prefill_qkv(cfg)
     out = FNS[mode](q.to(DEV), k.to(DEV), v.to(DEV), cfg.n, cfg.scale)
-    ref = oracle.prefill_ref(si.bits(q), si.bits(k), si.bits(v), cfg.n, mode, cfg.scale)
-    assert_close(f64(out), ref, f"tiny mode={mode}")
+    ref, ref_abs = prefill_pair(si.bits(q), si.bits(k), si.bits(v), cfg.n, mode, cfg.scale)
+    assert_close(f64(out), ref, f"tiny mode={mode}", ref_abs=ref_abs)
 
 
 SWEEP = [
@@ -183,8 +184,8 @@ def test_prefill_sweep(n, B, L, Hq, Hkv, D, mode):
     k = _rand((B, N, Hkv, D), 1.0, seed + 1, "cpu")
     v = _rand((B, N, Hkv, D), 1.0, seed + 2, "cpu")
     out = FNS[mode](q.to(DEV), k.to(DEV), v.to(DEV), n, 1.0)
-    ref = oracle.prefill_ref(si.bits(q), si.bits(k), si.bits(v), n, mode, 1.0)
-    assert_close(f64(out), ref, f"sweep n={n} L={L} H={Hq}/{Hkv} D={D} mode={mode}")
+    ref, ref_abs = prefill_pair(si.bits(q), si.bits(k), si.bits(v), n, mode, 1.0)
+    assert_close(f64(out), ref, f"sweep n={n} L={L} H={Hq}/{Hkv} D={D} mode={mode}", ref_abs=ref_abs)
 
 
 # sliding-window mixing: n, B, L, Hq, Hkv, D, W (W in interleaved positions)
@@ -209,8 +210,8 @@ def test_prefill_window_sweep(n, B, L, Hq, Hkv, D, W):
     k = _rand((B, N, Hkv, D), 1.0, seed + 1, "cpu")
     v = _rand((B, N, Hkv, D), 1.0, seed + 2, "cpu")
     out = hd.mix_attn_window(q.to(DEV), k.to(DEV), v.to(DEV), n, 1.0, W)
-    ref = oracle.prefill_ref(si.bits(q), si.bits(k), si.bits(v), n, MIX, 1.0, window=W)
-    assert_close(f64(out), ref, f"window W={W} n={n} L={L} H={Hq}/{Hkv} D={D}")
+    ref, ref_abs = prefill_pair(si.bits(q), si.bits(k), si.bits(v), n, MIX, 1.0, window=W)
+    assert_close(f64(out), ref, f"window W={W} n={n} L={L} H={Hq}/{Hkv} D={D}", ref_abs=ref_abs)
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -223,15 +224,15 @@ def test_prefill_window_scale_modes(D):
     k = _rand((B, N, Hkv, D), 1.0, seed + 1, "cpu")
     v = _rand((B, N, Hkv, D), 1.0, seed + 2, "cpu")
     scale = D ** -0.5
-    ref = oracle.prefill_ref(si.bits(q), si.bits(k), si.bits(v), n, MIX, scale, window=W)
+    ref, ref_abs = prefill_pair(si.bits(q), si.bits(k), si.bits(v), n, MIX, scale, window=W)
     kd, vd = k.to(DEV), v.to(DEV)
     out0 = hd.mix_attn_window(q.to(DEV), kd, vd, n, scale, W)
-    assert_close(f64(out0), ref, f"window any-scale D={D}")
+    assert_close(f64(out0), ref, f"window any-scale D={D}", ref_abs=ref_abs)
     out1 = hd.mix_attn_window((q.float() * scale).to(torch.bfloat16).to(DEV), kd, vd, n, 1.0, W)
-    assert_close(f64(out1), ref, f"window unit-scale D={D}")
+    assert_close(f64(out1), ref, f"window unit-scale D={D}", ref_abs=ref_abs)
     out2 = hd.mix_attn_window((q.float() * (scale * si.LOG2E)).to(torch.bfloat16).to(DEV), kd, vd,
                               n, si.LN2, W)
-    assert_close(f64(out2), ref, f"window log2 units D={D}")
+    assert_close(f64(out2), ref, f"window log2 units D={D}", ref_abs=ref_abs)
 
 
 def test_prefill_window_one_returns_v_exactly():
@@ -267,10 +268,10 @@ def test_prefill_window_full_size_sampled():
     rows = np.unique(np.concatenate([rows, [W - 2, W - 1, W, W + 1, W + 63, W + 64]]))
     G = cfg.Hq // cfg.Hkv
     heads = sorted({0, G - 1, G, cfg.Hq - 1})
-    ref = oracle.prefill_ref(si.bits(q[:1].cpu()), si.bits(k[:1].cpu()), si.bits(v[:1].cpu()),
-                             cfg.n, MIX, cfg.scale, rows=rows, heads=heads, window=W)
+    ref, ref_abs = prefill_pair(si.bits(q[:1].cpu()), si.bits(k[:1].cpu()), si.bits(v[:1].cpu()),
+                                cfg.n, MIX, cfg.scale, rows=rows, heads=heads, window=W)
     got = f64(out[:1, torch.as_tensor(rows, device=DEV)][:, :, heads].cpu())
-    assert_close(got, ref, f"n4 window {W} sampled")
+    assert_close(got, ref, f"n4 window {W} sampled", ref_abs=ref_abs)
 
 
 # ---------------------------------------------------------------------------
@@ -324,9 +325,9 @@ def test_attn_bwd_sweep(n, B, L, Hq, Hkv, D, mode):
     rq, rk, rv, _ = oracle.prefill_backward_ref(si.bits(q.cpu()), si.bits(k.cpu()), si.bits(v.cpu()),
                                                 si.bits(do.cpu()), n, mode, scale)
     what = f"bwd n={n} L={L} H={Hq}/{Hkv} D={D} mode={mode}"
-    assert_close(f64(dq.cpu()), rq, "dq " + what)
-    assert_close(f64(dk.cpu()), rk, "dk " + what)
-    assert_close(f64(dv.cpu()), rv, "dv " + what)
+    assert_close(f64(dq.cpu()), rq, "dq " + what, c10=False)
+    assert_close(f64(dk.cpu()), rk, "dk " + what, c10=False)
+    assert_close(f64(dv.cpu()), rv, "dv " + what, c10=False)
 
 
 def test_attn_bwd_single_position():
@@ -359,9 +360,9 @@ def test_attn_bwd_n4_full_size_one_group(mode):
     rq, rk, rv, _ = oracle.prefill_backward_ref(si.bits(q[:1].cpu()), si.bits(k[:1].cpu()),
                                                 si.bits(v[:1].cpu()), si.bits(do[:1].cpu()),
                                                 cfg.n, mode, cfg.scale, heads=[0])
-    assert_close(f64(dq[:1, :, :G].cpu()), rq, f"n4 dq mode={mode}")
-    assert_close(f64(dk[:1, :, :1].cpu()), rk, f"n4 dk mode={mode}")
-    assert_close(f64(dv[:1, :, :1].cpu()), rv, f"n4 dv mode={mode}")
+    assert_close(f64(dq[:1, :, :G].cpu()), rq, f"n4 dq mode={mode}", c10=False)
+    assert_close(f64(dk[:1, :, :1].cpu()), rk, f"n4 dk mode={mode}", c10=False)
+    assert_close(f64(dv[:1, :, :1].cpu()), rv, f"n4 dv mode={mode}", c10=False)
 
 
 WIN_BWD_SWEEP = [
@@ -394,9 +395,9 @@ def test_attn_window_training_sweep(n, B, L, Hq, Hkv, D, W):
                                                  si.bits(do.cpu()), n, MIX, scale, window=W)
     what = f"window bwd n={n} L={L} H={Hq}/{Hkv} D={D} W={W}"
     _assert_lse(lse.permute(0, 2, 1).cpu().numpy().astype(np.float64), rl, "lse " + what)
-    assert_close(f64(dq.cpu()), rq, "dq " + what)
-    assert_close(f64(dk.cpu()), rk, "dk " + what)
-    assert_close(f64(dv.cpu()), rv, "dv " + what)
+    assert_close(f64(dq.cpu()), rq, "dq " + what, c10=False)
+    assert_close(f64(dk.cpu()), rk, "dk " + what, c10=False)
+    assert_close(f64(dv.cpu()), rv, "dv " + what, c10=False)
 
 
 def test_attn_window_one_training():
@@ -448,9 +449,9 @@ def test_attn_window_training_n4_full_size_one_group():
     rq, rk, rv, _ = oracle.prefill_backward_ref(si.bits(q[:1].cpu()), si.bits(k[:1].cpu()),
                                                 si.bits(v[:1].cpu()), si.bits(do[:1].cpu()),
                                                 cfg.n, MIX, cfg.scale, window=W, heads=[0])
-    assert_close(f64(dq[:1, :, :G].cpu()), rq, "n4 window dq")
-    assert_close(f64(dk[:1, :, :1].cpu()), rk, "n4 window dk")
-    assert_close(f64(dv[:1, :, :1].cpu()), rv, "n4 window dv")
+    assert_close(f64(dq[:1, :, :G].cpu()), rq, "n4 window dq", c10=False)
+    assert_close(f64(dk[:1, :, :1].cpu()), rk, "n4 window dk", c10=False)
+    assert_close(f64(dv[:1, :, :1].cpu()), rv, "n4 window dv", c10=False)
 
 
 def test_attn_bwd_deterministic():
@@ -482,15 +483,15 @@ def test_prefill_nonunit_scale(D, mode):
     v = _rand((B, N, Hkv, D), 1.0, seed + 2, "cpu")
     scale = D ** -0.5
     out = FNS[mode](q.to(DEV), k.to(DEV), v.to(DEV), n, scale)
-    ref = oracle.prefill_ref(si.bits(q), si.bits(k), si.bits(v), n, mode, scale)
-    assert_close(f64(out), ref, f"scale={scale:.4f} D={D} mode={mode}")
+    ref, ref_abs = prefill_pair(si.bits(q), si.bits(k), si.bits(v), n, mode, scale)
+    assert_close(f64(out), ref, f"scale={scale:.4f} D={D} mode={mode}", ref_abs=ref_abs)
     # the same product through the unit-scale kernel: Q pre-scaled on the host
     out1 = FNS[mode]((q.float() * scale).to(torch.bfloat16).to(DEV), k.to(DEV), v.to(DEV), n, 1.0)
-    assert_close(f64(out1), ref, f"pre-scaled D={D} mode={mode}")
+    assert_close(f64(out1), ref, f"pre-scaled D={D} mode={mode}", ref_abs=ref_abs)
     # and with log2(e) folded in as well: scores arrive in log2 units
     out2 = FNS[mode]((q.float() * (scale * si.LOG2E)).to(torch.bfloat16).to(DEV), k.to(DEV), v.to(DEV),
                      n, si.LN2)
-    assert_close(f64(out2), ref, f"log2 units D={D} mode={mode}")
+    assert_close(f64(out2), ref, f"log2 units D={D} mode={mode}", ref_abs=ref_abs)
 
 
 def _sample_rows(N, n, count, seed):
@@ -517,10 +518,10 @@ def test_prefill_full_size_sampled(cfg, layer, mode):
     G = cfg.Hq // cfg.Hkv
     heads = sorted({0, G - 1, G, cfg.Hq - 1})
     for b in range(cfg.B):
-        ref = oracle.prefill_ref(si.bits(q[b:b + 1]), si.bits(k[b:b + 1]), si.bits(v[b:b + 1]),
-                                 cfg.n, mode, cfg.scale, rows=rows, heads=heads)
+        ref, ref_abs = prefill_pair(si.bits(q[b:b + 1]), si.bits(k[b:b + 1]), si.bits(v[b:b + 1]),
+                                    cfg.n, mode, cfg.scale, rows=rows, heads=heads)
         got = f64(out[b:b + 1][:, torch.as_tensor(rows, device=DEV)][:, :, heads])
-        assert_close(got, ref, f"{cfg.name} b={b} mode={mode}")
+        assert_close(got, ref, f"{cfg.name} b={b} mode={mode}", ref_abs=ref_abs)
 
 
 def test_prefill_literal_scaling_reading():
@@ -530,9 +531,9 @@ def test_prefill_literal_scaling_reading():
     q, k, v = si.prefill_qkv(cfg, device=DEV, q_std=s, kv_std=s, B=1, L=256)
     for mode in (WITHIN, MIX):
         out = FNS[mode](q, k, v, cfg.n, 1.0)
-        ref = oracle.prefill_ref(si.bits(q), si.bits(k), si.bits(v), cfg.n, mode, 1.0,
-                                 heads=[0, 5, 31])
-        assert_close(f64(out[:, :, [0, 5, 31]]), ref, f"literal scaling mode={mode}")
+        ref, ref_abs = prefill_pair(si.bits(q), si.bits(k), si.bits(v), cfg.n, mode, 1.0,
+                                    heads=[0, 5, 31])
+        assert_close(f64(out[:, :, [0, 5, 31]]), ref, f"literal scaling mode={mode}", ref_abs=ref_abs)
 
 
 @pytest.mark.parametrize("mode", [WITHIN, MIX])
@@ -543,8 +544,8 @@ def test_prefill_peaked_softmax(mode):
     k = _rand((1, n * L, Hkv, D), 1.0, 32, "cpu")
     v = _rand((1, n * L, Hkv, D), 1.0, 33, "cpu")
     out = FNS[mode](q.to(DEV), k.to(DEV), v.to(DEV), n, 1.0)
-    ref = oracle.prefill_ref(si.bits(q), si.bits(k), si.bits(v), n, mode, 1.0)
-    assert_close(f64(out), ref, "peaked")
+    ref, ref_abs = prefill_pair(si.bits(q), si.bits(k), si.bits(v), n, mode, 1.0)
+    assert_close(f64(out), ref, "peaked", ref_abs=ref_abs)
 
 
 def test_prefill_exact_pins():
@@ -582,7 +583,8 @@ def test_prefill_stream_one_hot_pin():
     o = hd.stream_attn(q, k, v, n, 1.0)
     want = torch.zeros((1, N, Hq, D), dtype=torch.float64, device=DEV)
     want[0, pos, :, pos % n] = 1.0
-    assert_close(o.double().cpu().numpy(), want.cpu().numpy(), "one-hot")
+    # sum_j p_j |v_j| is the same one-hot vector
+    assert_close(o.double().cpu().numpy(), want.cpu().numpy(), "one-hot", ref_abs=want.cpu().numpy())
 
 
 @pytest.mark.parametrize("mode", [WITHIN, MIX])
@@ -594,13 +596,16 @@ def test_prefill_k_zero_prefix_means(mode):
     v = _rand((1, N, Hkv, D), 1.0, 62)
     o = FNS[mode](q, k, v, n, 1.0)
     vf = f64(v)[0]
-    if mode == MIX:
-        want = np.cumsum(vf, axis=0) / np.arange(1, N + 1)[:, None, None]
-    else:
-        want = np.empty_like(vf)
+
+    def prefix_means(x):
+        if mode == MIX:
+            return np.cumsum(x, axis=0) / np.arange(1, N + 1)[:, None, None]
+        m = np.empty_like(x)
         for s in range(n):
-            want[s::n] = np.cumsum(vf[s::n], axis=0) / np.arange(1, L + 1)[:, None, None]
-    assert_close(f64(o)[0], want, "prefix means")
+            m[s::n] = np.cumsum(x[s::n], axis=0) / np.arange(1, L + 1)[:, None, None]
+        return m
+
+    assert_close(f64(o)[0], prefix_means(vf), "prefix means", ref_abs=prefix_means(np.abs(vf)))
 
 
 def test_negative_controls_fail_the_bar():
@@ -644,9 +649,10 @@ def _decode_case(cfg, S, T, tb, mode, seqs=None, max_tokens=None, device=DEV, wi
                                           si.bits(vn[sl]), tbh[sl], cfg.n)
         assert np.array_equal(si.bits(kc[sl]), k2), f"k append seq {qi}"
         assert np.array_equal(si.bits(vc[sl]), v2), f"v append seq {qi}"
-        ref = oracle.decode_ref(si.bits(qn[sl]), k2, v2, tbh[sl], cfg.n, mode, cfg.scale,
-                                window=window)
-        assert_close(f64(out[sl]), ref, f"decode seq {qi} T={tbh[qi]} mode={mode} window={window}")
+        ref, ref_abs = decode_pair(si.bits(qn[sl]), k2, v2, tbh[sl], cfg.n, mode, cfg.scale,
+                                   window=window)
+        assert_close(f64(out[sl]), ref, f"decode seq {qi} T={tbh[qi]} mode={mode} window={window}",
+                     ref_abs=ref_abs)
     return out
 
 
@@ -727,8 +733,8 @@ def test_decode_long_context_sampled(mode):
                                           si.bits(vn[sl]), tbh[sl], cfg.n)
         assert np.array_equal(si.bits(kc[sl]), k2), f"k append seq {qi}"
         assert np.array_equal(si.bits(vc[sl]), v2), f"v append seq {qi}"
-        ref = oracle.decode_ref(si.bits(qn[sl]), k2, v2, tbh[sl], cfg.n, mode, cfg.scale)
-        assert_close(f64(out[sl]), ref, f"long decode seq {qi} T={tbh[qi]} mode={mode}")
+        ref, ref_abs = decode_pair(si.bits(qn[sl]), k2, v2, tbh[sl], cfg.n, mode, cfg.scale)
+        assert_close(f64(out[sl]), ref, f"long decode seq {qi} T={tbh[qi]} mode={mode}", ref_abs=ref_abs)
     del qn, kn, vn, kc, vc, tbt, out
     torch.cuda.empty_cache()
 
@@ -898,8 +904,8 @@ def test_decode_paged_oracle_on_gathered_pages():
     C = kc.shape[1]
     k2 = oracle.gather_pages_ref(si.bits(kp), pt.cpu().numpy(), C)
     v2 = oracle.gather_pages_ref(si.bits(vp), pt.cpu().numpy(), C)
-    ref = oracle.decode_ref(si.bits(qn), k2, v2, tbt.cpu().numpy(), cfg.n, MIX, cfg.scale, window=200)
-    assert_close(f64(out), ref, "paged decode vs oracle")
+    ref, ref_abs = decode_pair(si.bits(qn), k2, v2, tbt.cpu().numpy(), cfg.n, MIX, cfg.scale, window=200)
+    assert_close(f64(out), ref, "paged decode vs oracle", ref_abs=ref_abs)
 
 
 def test_decode_stack_graph_replays_match_eager():
@@ -981,8 +987,8 @@ def test_decode_stack_three_layer_kinds():
         vc = oracle.gather_pages_ref(vp0[i], pth, C)
         k2, v2 = oracle.decode_append_ref(kc, vc, si.bits(ks[i]), si.bits(vs[i]), tbh, n)
         mode, window = st.layer_call(i)
-        ref = oracle.decode_ref(si.bits(qs[i]), k2, v2, tbh, n, mode, D ** -0.5, window=window)
-        assert_close(f64(outs[i]), ref, f"stack layer {i} ({kind})")
+        ref, ref_abs = decode_pair(si.bits(qs[i]), k2, v2, tbh, n, mode, D ** -0.5, window=window)
+        assert_close(f64(outs[i]), ref, f"stack layer {i} ({kind})", ref_abs=ref_abs)
 
 
 def test_decode_idempotent_append_and_modes_share_cache():
@@ -1007,4 +1013,5 @@ def test_decode_matches_prefill_tail_on_gpu(mode):
     qp = _rand((1, N, Hq, D), 1.0, 81)
     qp[0, T * n:] = qn[0]
     pre = FNS[mode](qp, kc[:, :N].contiguous(), vc[:, :N].contiguous(), n, cfg.scale)
-    assert_close(f64(out[0]), f64(pre[0, T * n:]), "decode vs prefill tail")
+    # two GPU results, each with its own bf16 roundings: the base bar only
+    assert_close(f64(out[0]), f64(pre[0, T * n:]), "decode vs prefill tail", c10=False)

@@ -292,6 +292,37 @@ def test_backward_ref_sums_query_heads_into_kv_heads():
         np.testing.assert_allclose(dk[0, :, g], acc, atol=1e-13)
 
 
+@pytest.mark.parametrize("n,L,Hq,Hkv,mode,window", [(2, 5, 4, 2, MIX, None), (3, 4, 6, 2, WITHIN, None),
+                                                    (2, 6, 8, 2, MIX, 5), (1, 9, 3, 1, MIX, None)])
+def test_backward_ref_gqa_matches_autograd_through_repeated_kv(n, L, Hq, Hkv, mode, window):
+    """prefill_backward_ref (every head, the query heads of a group summed
+    into its dK / dV) against float64 torch autograd of a whole multi-head
+    layer whose K and V reach the heads through repeat_interleave over the
+    head axis (query head h reads KV head h // (Hq / Hkv), reading R6):
+    autograd sums the repeated copies' gradients by itself, with no per-head
+    loop of the oracle's."""
+    rng = np.random.default_rng(1000 + 10 * n + L + Hq)
+    D, scale = 8, 0.55
+    q, k, v = _qkv(rng, 1, n, L, Hq, Hkv, D)
+    do = _rand_bits(rng, (1, n * L, Hq, D))
+    dq, dk, dv, lse = oracle.prefill_backward_ref(q, k, v, do, n, mode, scale, window=window)
+    N, G = n * L, Hq // Hkv
+    qt = torch.tensor(_f(q)[0], requires_grad=True)          # [N, Hq, D]
+    kt = torch.tensor(_f(k)[0], requires_grad=True)          # [N, Hkv, D]
+    vt = torch.tensor(_f(v)[0], requires_grad=True)
+    kr = kt.repeat_interleave(G, dim=1)                     # [N, Hq, D]
+    vr = vt.repeat_interleave(G, dim=1)
+    mask = torch.tensor(sfa.visible(np.arange(N)[:, None], np.arange(N)[None, :], n, mode, window))
+    s = scale * torch.einsum("ihd,jhd->hij", qt, kr)
+    s = s.masked_fill(~mask[None], float("-inf"))
+    o = torch.einsum("hij,jhd->ihd", torch.softmax(s, dim=2), vr)
+    o.backward(torch.tensor(_f(do)[0]))
+    np.testing.assert_allclose(dq[0], qt.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk[0], kt.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv[0], vt.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[0], torch.logsumexp(s, dim=2).T.detach().numpy(), rtol=0, atol=1e-12)
+
+
 # ---------------------------------------------------------------------------
 # sliding-window mixing (reading R13)
 # ---------------------------------------------------------------------------
