@@ -129,6 +129,22 @@ def bench_prefill(args, torch, hd, si):
     t_exp = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     t_w = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     t_m = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    fw = attn_flops(cfg.B, cfg.n, cfg.L, cfg.Hq, cfg.D, "within")
+    fm = attn_flops(cfg.B, cfg.n, cfg.L, cfg.Hq, cfg.D, "mix")
+    exp_bytes = cfg.B * cfg.N * cfg.hidden * 2 * 2 + cfg.B * cfg.L * 4
+    res = dict(cfg=cfg, ms_step=ms_step, t_exp=t_exp, t_w=t_w, t_m=t_m, fw=fw, fm=fm,
+               exp_bytes=exp_bytes)
+    if not args.only_step:
+        res.update(bench_prefill_extras(args, torch, hd, si, cfg, ids, tab, q, k, v, x, ow, om))
+    del ids, tab, q, k, v, x, ow, om
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_prefill_extras(args, torch, hd, si, cfg, ids, tab, q, k, v, x, ow, om):
+    """Kernels outside the step, on the step's n4 inputs: the sliding-window
+    mixing layer, final-stream rows, cyclic replication and training."""
+    dev = q.device
     # the sliding-window mixing layer (not part of the step): same inputs
     for _ in range(3):
         hd.mix_attn_window(q, k, v, cfg.n, cfg.scale, WINDOW, out=om)
@@ -185,14 +201,72 @@ def bench_prefill(args, torch, hd, si):
         bwd[name] = (t_f, ew[0].elapsed_time(ew[1]) / reps)
         del o_, lse, grads
 
-    fw = attn_flops(cfg.B, cfg.n, cfg.L, cfg.Hq, cfg.D, "within")
-    fm = attn_flops(cfg.B, cfg.n, cfg.L, cfg.Hq, cfg.D, "mix")
     fmw = attn_flops(cfg.B, cfg.n, cfg.L, cfg.Hq, cfg.D, "mix", WINDOW)
-    exp_bytes = cfg.B * cfg.N * cfg.hidden * 2 * 2 + cfg.B * cfg.L * 4
-    res = dict(cfg=cfg, ms_step=ms_step, t_exp=t_exp, t_w=t_w, t_m=t_m, fw=fw, fm=fm,
-               exp_bytes=exp_bytes, t_mw=t_mw, fmw=fmw, t_fs=t_fs, fs_bytes=fs_bytes,
-               t_cr=t_cr, cr_bytes=cr_bytes, bwd=bwd)
-    del ids, tab, q, k, v, x, ow, om, fsr
+    del fsr, do
+    return dict(t_mw=t_mw, fmw=fmw, t_fs=t_fs, fs_bytes=fs_bytes, t_cr=t_cr, cr_bytes=cr_bytes,
+                bwd=bwd)
+
+
+def _time_calls(torch, fn, reps, warm=2):
+    """Mean ms of fn() over reps back-to-back calls (HIP events on the
+    current stream, which is the one the library launches on)."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = _events(2)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def bench_long_prefill(args, torch, hd, si):
+    """The long-context workload: n=4, B=1, L=8192 (nL=32768), 64/4 heads,
+    D=128; the within-stream and mixing layers, each timed on its own."""
+    cfg = si.LONG
+    q, k, v = si.prefill_qkv(cfg, device=torch.device("cuda"))
+    out = torch.empty_like(q)
+    reps = max(2, args.steps // 4)
+    res = {"workload": "long: n=4, batch 1, L=8192 tokens (nL=32768), 64 query / 4 KV heads "
+                       "(GQA 16:1), head_dim 128, Q ~ N(0,1) log2(e)/sqrt(128), K, V ~ N(0,1); "
+                       "scores in log2 units (scale ln 2)"}
+    for name, fn in (("within", hd.stream_attn), ("mix", hd.mix_attn)):
+        ms = _time_calls(torch, lambda: fn(q, k, v, cfg.n, cfg.scale, out=out), reps, warm=1)
+        fl = attn_flops(cfg.B, cfg.n, cfg.L, cfg.Hq, cfg.D, name)
+        tf = fl / (ms * 1e-3) / 1e12
+        res[name] = {"ms": round(ms, 4), "useful_gflop": round(fl / 1e9, 2), "achieved": round(tf, 2),
+                     "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS, "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    del q, k, v, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_scale_modes(args, torch, hd, si):
+    """The n4 layers with the softmax scale carried other ways than the step's
+    log2-unit scores: Q ~ N(0,1)/sqrt(128) with scale 1 (the scale folded into
+    Q only) and unscaled Q ~ N(0,1) with scale 1/sqrt(128) passed to the call.
+    Same FLOPs and precision; the kernel's exponent argument takes one more
+    operand (a literal log2(e), or the scale from the arguments)."""
+    import math
+    cfg = si.N4
+    dev = torch.device("cuda")
+    reps = max(3, args.steps // 2)
+    res = {}
+    for name, q_std, scale in (("unit_scale", 1 / math.sqrt(cfg.D), 1.0),
+                               ("any_scale", 1.0, 1 / math.sqrt(cfg.D))):
+        q, k, v = si.prefill_qkv(cfg, device=dev, q_std=q_std)
+        out = torch.empty_like(q)
+        entry = {"q_std": round(q_std, 6), "softmax_scale": round(scale, 6)}
+        for mode, fn in (("within", hd.stream_attn), ("mix", hd.mix_attn)):
+            ms = _time_calls(torch, lambda: fn(q, k, v, cfg.n, scale, out=out), reps)
+            fl = attn_flops(cfg.B, cfg.n, cfg.L, cfg.Hq, cfg.D, mode)
+            tf = fl / (ms * 1e-3) / 1e12
+            entry[mode] = {"ms": round(ms, 4), "achieved": round(tf, 2), "unit": "TFLOP/s",
+                           "peak": PEAK_BF16_TFLOPS, "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+        res[name] = entry
+        del q, k, v, out
     torch.cuda.empty_cache()
     return res
 
@@ -374,41 +448,136 @@ def bench_stack(args, torch, hd, si):
     }
 
 
-def cpu_baseline(si, budget_s):
-    """Oracle on a bounded sample of the n=4 workload: the last query rows of
-    batch 0 (the most expensive ones), all 32 heads, both layers, growing the
-    sample until ``budget_s`` seconds of CPU work have been spent."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:
+        return os.cpu_count()
+
+
+def _oracle_prefill_sample(si, oracle, cfg, layer_modes, budget_s, block=64, heads=None):
+    """Oracle on the last query rows of batch 0 (the most expensive ones),
+    every head (or the given ones), every layer in layer_modes [(layer,
+    mode)], growing the sample until budget_s seconds have been spent.
+    Returns (useful FLOPs, wall s, CPU s, rows)."""
     import numpy as np
-    import oracle
-    cfg = si.N4
-    q, k, v = si.prefill_qkv(cfg, B=1)
-    qb, kb, vb = si.bits(q), si.bits(k), si.bits(v)
+    bits = {}
+    for layer, _ in layer_modes:
+        if layer not in bits:
+            q, k, v = si.prefill_qkv(cfg, layer=layer, B=1)
+            bits[layer] = (si.bits(q), si.bits(k), si.bits(v))
+            del q, k, v
     N = cfg.N
     flops = 0
     rows_done = 0
-    t0 = time.perf_counter()
-    block = 64
+    c0, t0 = time.process_time(), time.perf_counter()
     while time.perf_counter() - t0 < budget_s and rows_done < N:
         hi = N - rows_done
         rows = np.arange(hi - block, hi)
-        for mode in (oracle.WITHIN, oracle.MIX):
-            oracle.prefill_ref(qb, kb, vb, cfg.n, mode, cfg.scale, rows=rows)
+        for layer, mode in layer_modes:
+            qb, kb, vb = bits[layer]
+            oracle.prefill_ref(qb, kb, vb, cfg.n, mode, cfg.scale, rows=rows, heads=heads)
             keys = (rows // cfg.n + 1) if mode == oracle.WITHIN else (rows + 1)
-            flops += 4 * cfg.D * cfg.Hq * int(keys.sum())
+            flops += 4 * cfg.D * (cfg.Hq if heads is None else len(heads)) * int(keys.sum())
         rows_done += block
+    return flops, time.perf_counter() - t0, time.process_time() - c0, rows_done
+
+
+def cpu_baseline(si, budget_s):
+    """The float64 oracle as it stands, timed on the host cores.  The reported
+    value is a bounded sample of the n4 workload (the last query rows of
+    batch 0, all 32 heads, both layers, grown until ``budget_s`` seconds of
+    work).  ``per_config`` times every workload the same way: the tiny one in
+    full (with all BLAS threads and with one), the others on bounded samples
+    whose useful rate gives an estimate of the full workload's oracle time."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    W, M = oracle.WITHIN, oracle.MIX
+    threads = _blas_threads()
+    per = {}
+
+    # tiny: the whole workload (both layers), all threads and a single thread
+    cfg = si.TINY
+    q, k, v = si.prefill_qkv(cfg)
+    qb, kb, vb = si.bits(q), si.bits(k), si.bits(v)
+    fl = sum(4 * cfg.D * cfg.Hq * cfg.B * oracle.count_pairs(cfg.N, cfg.n, m) for m in (W, M))
+    for key, lim in (("all_threads", None), ("single_thread", 1)):
+        with threadpool_limits(lim):
+            t0 = time.perf_counter()
+            for m in (W, M):
+                oracle.prefill_ref(qb, kb, vb, cfg.n, m, cfg.scale)
+            dt = time.perf_counter() - t0
+        per.setdefault("tiny", {"sample": "whole workload, both layers", "useful_gflop": round(fl / 1e9, 6)})
+        per["tiny"][key] = {"s": round(dt, 4), "gflop_per_s": round(fl / dt / 1e9, 3),
+                            "threads": threads if lim is None else 1}
+
+    # n4 (the reported value)
+    cfg = si.N4
+    flops, dt, cpu_s, rows = _oracle_prefill_sample(si, oracle, cfg, [(0, W), (0, M)], budget_s)
+    full = sum(4 * cfg.D * cfg.Hq * cfg.B * oracle.count_pairs(cfg.N, cfg.n, m) for m in (W, M))
+    rate = flops / dt
+    per["n4"] = {"sample": f"batch 0, all heads, last {rows} of {cfg.N} query rows, both layers",
+                 "s": round(dt, 2), "gflop_per_s": round(rate / 1e9, 3),
+                 "est_full_workload_s": round(full / rate, 1)}
+    value = rate / 1e12
+    main = {"dt": dt, "cpu_s": cpu_s, "rows": rows, "flops": flops}
+
+    # n8 stack and long context: bounded samples
+    side = max(2.0, budget_s / 4)
+    for name, cfg, lm, hs in (("n8stack", si.N8STACK, [(0, W), (3, M)], None),
+                              ("long", si.LONG, [(0, W), (0, M)], list(range(0, 64, 8)))):
+        flops, dt, _, rows = _oracle_prefill_sample(si, oracle, cfg, lm, side, block=32, heads=hs)
+        if name == "n8stack":
+            full = (3 * 4 * cfg.D * cfg.Hq * cfg.B * cfg.n * cfg.L * (cfg.L + 1) // 2 +
+                    4 * cfg.D * cfg.Hq * cfg.B * cfg.N * (cfg.N + 1) // 2)
+        else:
+            full = (4 * cfg.D * cfg.Hq * cfg.B * (cfg.n * cfg.L * (cfg.L + 1) // 2 + cfg.N * (cfg.N + 1) // 2))
+        rate = flops / dt
+        per[name] = {"sample": f"batch 0, {'all heads' if hs is None else f'heads {hs}'}, last {rows} "
+                               f"of {cfg.N} query rows, layers {[l for l, _ in lm]}",
+                     "s": round(dt, 2), "gflop_per_s": round(rate / 1e9, 3),
+                     "est_full_workload_s": round(full / rate, 1)}
+
+    # decode: a few sequences of the decode workload's shape, both modes
+    dc = si.DECODE
+    S = 2
+    qn, kn, vn, kc, vc, tb = si.decode_inputs(dc, S=S)
+    t0 = time.perf_counter()
+    k2, v2 = oracle.decode_append_ref(si.bits(kc), si.bits(vc), si.bits(kn), si.bits(vn), tb.numpy(), dc.n)
+    nbytes = 0
+    for m in (W, M):
+        oracle.decode_ref(si.bits(qn), k2, v2, tb.numpy(), dc.n, m, dc.scale)
+        nbytes += S * (dc.T + 1) * dc.n * dc.Hkv * dc.D * 2 * 2
     dt = time.perf_counter() - t0
-    threads = None
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-    except Exception:
-        threads = os.cpu_count()
+    full_bytes = 2 * dc.S * (dc.T + 1) * dc.n * dc.Hkv * dc.D * 2 * 2
+    per["decode"] = {"sample": f"{S} sequences of 4096 tokens x 4 streams, append + both modes",
+                     "s": round(dt, 2), "gb_per_s": round(nbytes / dt / 1e9, 3),
+                     "est_full_workload_s": round(full_bytes / (nbytes / dt), 1)}
+    del qn, kn, vn, kc, vc, k2, v2
+
     return {
-        "value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+        "value": round(value, 6), "unit": "TFLOP/s", "cores": threads,
         "kind": "oracle",
-        "sample": f"n4 workload, batch 0, all 32 heads, last {rows_done} query rows of the "
+        "sample": f"n4 workload, batch 0, all 32 heads, last {main['rows']} query rows of the "
                   f"4096 (within-stream and mixing layers), float64 NumPy oracle, "
-                  f"{dt:.1f} s wall, {flops / 1e9:.2f} useful GFLOP",
+                  f"{main['dt']:.1f} s wall, {main['flops'] / 1e9:.2f} useful GFLOP",
+        "cores_note": "cores = threads of the BLAS pool the oracle's products ran on; "
+                      "effective_cores = process CPU seconds / wall seconds of the n4 sample",
+        "effective_cores": round(main["cpu_s"] / main["dt"], 2),
+        "cpu_model": _cpu_model(),
+        "os_cpu_count": os.cpu_count(),
+        "per_config": per,
     }
 
 
@@ -417,10 +586,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-budget", type=float, default=15.0,
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of CPU oracle work for cpu_baseline (0 to skip)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--only-step", action="store_true",
+                    help="time the step, the long-context layers and the scale modes only "
+                         "(for counter profiles)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one plain device copy (negation) of MIB MiB, the "
                          "reference kernel for scaling HBM byte counters")
@@ -451,6 +623,14 @@ def main():
 
     pf = bench_prefill(args, torch, hd, si)
     print(f"[bench] prefill done: step {pf['ms_step']:.4f} ms", file=sys.stderr, flush=True)
+    longp = bench_long_prefill(args, torch, hd, si)
+    print(f"[bench] long prefill done: within {longp['within']['ms']:.3f} ms mix {longp['mix']['ms']:.3f} ms",
+          file=sys.stderr, flush=True)
+    modes = bench_scale_modes(args, torch, hd, si)
+    print("[bench] scale modes done", file=sys.stderr, flush=True)
+    if args.only_step:
+        args.no_decode = args.no_stack = True
+        args.cpu_budget = 0
     dec = None if args.no_decode else bench_decode(args, torch, hd, si)
     if dec:
         print(f"[bench] decode done: within {dec['within']:.4f} ms mix {dec['mix']:.4f} ms",
@@ -481,32 +661,35 @@ def main():
         "sfa_mix_attn": {"ms": round(pf["t_m"], 4), "bound": "mfma",
                          "achieved": round(pf["fm"] / (pf["t_m"] * 1e-3) / 1e12, 2),
                          "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS},
-        "sfa_mix_attn_window": {"ms": round(pf["t_mw"], 4), "bound": "mfma",
-                                "achieved": round(pf["fmw"] / (pf["t_mw"] * 1e-3) / 1e12, 2),
-                                "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS,
-                                "window": WINDOW, "useful_gflop": round(pf["fmw"] / 1e9, 3),
-                                "note": "sliding-window mixing layer, same n4 inputs; "
-                                        "not part of the step"},
-        "hd_final_stream_rows": {"ms": round(pf["t_fs"], 4), "bound": "hbm",
-                                 "achieved": round(pf["fs_bytes"] / (pf["t_fs"] * 1e-3) / 1e9, 1),
-                                 "unit": "GB/s", "peak": PEAK_HBM_GBS,
-                                 "note": "[2, 4096, 4096] -> [2, 1024, 4096]; not part of the step"},
-        **{f"sfa_attn_bwd_{name}": {
-            "ms": round(pf["bwd"][name][1], 4), "bound": "mfma",
-            "achieved": round(2.5 * pf[fk] / (pf["bwd"][name][1] * 1e-3) / 1e12, 2),
-            "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS,
-            "fwd_with_lse_ms": round(pf["bwd"][name][0], 4),
-            "note": "gradients dq, dk, dv of the n4 layer" + (f" (sliding window {WINDOW})"
-                                                                if name == "mix_window" else "")
-                    + "; useful work counted as 2.5x the forward's (five products per visible "
-                      "pair); not part of the step"}
-           for name, fk in (("within", "fw"), ("mix", "fm"), ("mix_window", "fmw"))},
-        "hd_cyclic_replicate": {"ms": round(pf["t_cr"], 4), "bound": "hbm",
-                                "achieved": round(pf["cr_bytes"] / (pf["t_cr"] * 1e-3) / 1e9, 1),
-                                "unit": "GB/s", "peak": PEAK_HBM_GBS,
-                                "note": "2 -> 4 tables of 151936 x 4096 in place (2.49 GB read + "
-                                        "written); not part of the step"},
     }
+    if "t_mw" in pf:
+        kernels.update({
+            "sfa_mix_attn_window": {"ms": round(pf["t_mw"], 4), "bound": "mfma",
+                                    "achieved": round(pf["fmw"] / (pf["t_mw"] * 1e-3) / 1e12, 2),
+                                    "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS,
+                                    "window": WINDOW, "useful_gflop": round(pf["fmw"] / 1e9, 3),
+                                    "note": "sliding-window mixing layer, same n4 inputs; "
+                                            "not part of the step"},
+            "hd_final_stream_rows": {"ms": round(pf["t_fs"], 4), "bound": "hbm",
+                                     "achieved": round(pf["fs_bytes"] / (pf["t_fs"] * 1e-3) / 1e9, 1),
+                                     "unit": "GB/s", "peak": PEAK_HBM_GBS,
+                                     "note": "[2, 4096, 4096] -> [2, 1024, 4096]; not part of the step"},
+            **{f"sfa_attn_bwd_{name}": {
+                "ms": round(pf["bwd"][name][1], 4), "bound": "mfma",
+                "achieved": round(2.5 * pf[fk] / (pf["bwd"][name][1] * 1e-3) / 1e12, 2),
+                "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS,
+                "fwd_with_lse_ms": round(pf["bwd"][name][0], 4),
+                "note": "gradients dq, dk, dv of the n4 layer" + (f" (sliding window {WINDOW})"
+                                                                    if name == "mix_window" else "")
+                        + "; useful work counted as 2.5x the forward's (five products per visible "
+                          "pair); not part of the step"}
+               for name, fk in (("within", "fw"), ("mix", "fm"), ("mix_window", "fmw"))},
+            "hd_cyclic_replicate": {"ms": round(pf["t_cr"], 4), "bound": "hbm",
+                                    "achieved": round(pf["cr_bytes"] / (pf["t_cr"] * 1e-3) / 1e9, 1),
+                                    "unit": "GB/s", "peak": PEAK_HBM_GBS,
+                                    "note": "2 -> 4 tables of 151936 x 4096 in place (2.49 GB read + "
+                                            "written); not part of the step"},
+        })
     for kk in kernels.values():
         kk["frac"] = round(kk["achieved"] / kk["peak"], 4)
     line = {
@@ -539,6 +722,8 @@ def main():
         },
         "kernels": kernels,
     }
+    line["prefill_long"] = longp
+    line["scale_modes"] = modes
     if dec:
         line["decode"] = {
             "workload": "64 sequences x 4096 tokens x 4 streams cached (16388 live entries after "
