@@ -75,12 +75,67 @@ def _compile(src: str):
     return obj, _resources(remarks)
 
 
-def build(verbose: bool = True) -> str:
-    """Compile all sources and link the shared library; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
+# Host-side sanitizers for the checking build: AddressSanitizer and
+# UndefinedBehaviorSanitizer on the host code only (argument validation, plans,
+# launches); every flag is routed to the host pass, the device code is built
+# exactly as in the product library.
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined",
+                  "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+SANITIZED_BUILD = os.path.join(BUILD, "sanitized")
+SANITIZED_LIB = os.path.join(SANITIZED_BUILD, "_hd_sfa_sanitized.so")
+
+
+def build_sanitized(verbose: bool = True) -> str:
+    """Compile the library with host-side ASan + UBSan into
+    ``_build/sanitized/_hd_sfa_sanitized.so`` (for the CPU sanitizer test; it
+    needs the sanitizer runtime preloaded to be loaded)."""
+    os.makedirs(SANITIZED_BUILD, exist_ok=True)
+    srcs = _sources()
+
+    def one(src):
+        obj = os.path.join(SANITIZED_BUILD, os.path.basename(src) + ".o")
+        cmd = [hipcc(), *CFLAGS, *SANITIZE_FLAGS, "-c", src, "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stderr}")
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(one, srcs))
+    tmp = SANITIZED_LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-shared-libsan",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
+    os.replace(tmp, SANITIZED_LIB)
+    if verbose:
+        print(f"built {SANITIZED_LIB} (host ASan + UBSan)")
+    return SANITIZED_LIB
+
+
+def sanitizer_runtime() -> str:
+    """Path of the ASan runtime shared library of the compiler hipcc uses."""
+    clangxx = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang++")
+    if not os.path.exists(clangxx):
+        clangxx = "/opt/rocm/llvm/bin/clang++"
+    r = subprocess.run([clangxx, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                       text=True)
+    return r.stdout.strip()
+
+
+def _sources():
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     if not srcs:
         raise RuntimeError("no sources under csrc/")
+    return srcs
+
+
+def build(verbose: bool = True) -> str:
+    """Compile all sources and link the shared library; returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = _sources()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         done = list(ex.map(_compile, srcs))
     objs = [o for o, _ in done]
