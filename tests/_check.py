@@ -71,7 +71,9 @@ def assert_close(got, ref, what="", c10=True, ref_abs=None):
     ref = np.asarray(ref)
     scale = float(np.abs(ref).max()) if ref.size else 0.0
     ok2, ratio = maxabs_report(got, ref, ref_abs)
-    RECORD.append((what + ("" if ref_abs is None else " [rounding-aware]"), e, scale, ratio))
+    g64, r64 = np.asarray(got, dtype=np.float64), np.asarray(ref, dtype=np.float64)
+    base = float((np.abs(g64 - r64) / (ATOL + RTOL * np.abs(r64))).max()) if ref.size else 0.0
+    RECORD.append((what + ("" if ref_abs is None else " [rounding-aware]"), e, scale, ratio, base))
     assert ok, f"{what}: max abs err {e:.3e} (ref max {scale:.3e})"
     if c10:
         assert ok2, f"{what}: max-abs part violated, worst error/allowance {ratio:.3f} (ref max {scale:.3e})"

@@ -38,7 +38,8 @@ def pytest_sessionfinish(session, exitstatus):
         return
     import json
     from tests import _check
-    rows = [{"what": w, "max_abs_err": e, "max_abs_ref": r, "worst_err_over_maxabs_allowance": q}
-            for (w, e, r, q) in _check.RECORD]
+    rows = [{"what": w, "max_abs_err": e, "max_abs_ref": r, "worst_err_over_maxabs_allowance": q,
+             "worst_err_over_base_allowance": b}
+            for (w, e, r, q, b) in _check.RECORD]
     with open(path, "w") as f:
         json.dump(rows, f, indent=1)
