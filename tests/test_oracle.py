@@ -664,7 +664,9 @@ def test_planted_mistakes_are_caught(monkeypatch):
 
     for bad in (strict, no_stream, token_stream, anti):
         monkeypatch.setattr(sfa, "visible", bad)
-        assert not _pins_pass(), bad.__name__
+        # a planted mask can leave a row with no visible key (a NaN row)
+        with np.errstate(invalid="ignore"):
+            assert not _pins_pass(), bad.__name__
         monkeypatch.setattr(sfa, "visible", real)
 
     real_softmax = sfa._softmax_rows
