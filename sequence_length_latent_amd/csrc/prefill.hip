@@ -240,23 +240,32 @@ sfa_prefill_kernel(const PrefillArgs a) {
     };
     auto kbuf = [&](int t) { return smem + (t & 1) * TILE_B; };
     auto vbuf = [&](int t) { return smem + (NSTAGE + (t & 1)) * TILE_B; };
-    // Q fragments of an item, global -> this wave's LDS Q area: load e, lane
-    // l brings query row q0 + l%32 (clamped into the view; rows past its end
-    // are never stored), dims 16e + 8(l/32) .. +7, to +1024e + 16l.  The
-    // area is read once at the start of the item, so the next item's Q can be
-    // requested any time after that.
+    // Q of an item, global -> this wave's LDS Q area (its 32 rows), stored
+    // like a K tile: row-major with the XOR swizzle of the 16-byte chunks, so
+    // that every load instruction reads whole rows (4 rows of 256 bytes at
+    // head_dim 128) and the fragments are read back as the K operands are.
+    // Rows past the view end are clamped into it and never stored.  The
+    // area is read once at the start of the item, so the next item's Q can
+    // be requested any time after that.
     unsigned char* const qlds = smem + 2 * NSTAGE * TILE_B + wave * QW_B;
     auto issue_q = [&](uint32_t id) {
+        constexpr uint32_t CPR = ROWB / 16;    // 16-byte chunks per row
+        constexpr uint32_t RPL = 1024 / ROWB;  // rows per load instruction
+        static_assert(MQ / RPL == DSTEPS && MQ * ROWB == QW_B, "Q area layout");
         const uint32_t ln = lane_here();
         uint32_t q0;
         const uint64_t hoff = item_head(id, q0);
-        const char* src = reinterpret_cast<const char*>(
-            a.q + hoff + (uint64_t)min(q0 + (ln & 31u), a.len - 1u) * a.q_row);
+        const char* base = reinterpret_cast<const char*>(a.q + hoff);
+        const uint32_t j = ln / CPR, p = ln % CPR;
 #pragma unroll
-        for (int e = 0; e < DSTEPS; ++e)
+        for (uint32_t e = 0; e < (uint32_t)MQ / RPL; ++e) {
+            const uint32_t row = e * RPL + j;
+            const uint64_t qrow = min(q0 + row, a.len - 1u);
+            const char* src = base + qrow * (a.q_row * 2u) + ((p ^ swz<D>(row)) << 4);
             __builtin_amdgcn_global_load_lds(
-                (const void __attribute__((address_space(1)))*)(src + (2 * e + (ln >> 5)) * 16),
+                (const void __attribute__((address_space(1)))*)src,
                 (void __attribute__((address_space(3)))*)(qlds + e * 1024), 16, 0, 0);
+        }
     };
 
     // ---- output ----
@@ -553,7 +562,7 @@ sfa_prefill_kernel(const PrefillArgs a) {
         asm volatile("" ::: "memory");
 #pragma unroll
         for (int e = 0; e < DSTEPS; ++e)
-            qf[e] = *reinterpret_cast<const bf16x8*>(qlds + e * 1024 + lane * 16);
+            qf[e] = *reinterpret_cast<const bf16x8*>(qlds + koff[e]);   // row l32, chunk 2e + hh
 #pragma unroll
         for (int i = 0; i < DBLK; ++i) oacc[i] = f32x16{};
         m_run = -INFINITY;
