@@ -412,6 +412,14 @@ def bench_stack(args, torch, hd, si):
         for q, k, v in base:
             hd.mix_attn(q, k, v, 1, cfg.scale, out=out1)
 
+    # the n = 1 layer has as many work items as compute units: the key-split
+    # launch takes each item's key tiles in two halves on different workgroups
+    ws1 = hd.split_workspace(base[0][0], base[0][1], 1, hd.MIX)
+
+    def run_base_split():
+        for q, k, v in base:
+            hd.attn_split(q, k, v, 1, cfg.scale, hd.MIX, ws1, out=out1)
+
     def timeit(fn):
         t_end = time.perf_counter() + 0.2
         while time.perf_counter() < t_end:
@@ -427,19 +435,22 @@ def bench_stack(args, torch, hd, si):
 
     t_hd = timeit(run_hd)
     t_base = timeit(run_base)
+    t_base_split = timeit(run_base_split)
     q, k, v = layers[0]
     t_w = timeit(lambda: hd.stream_attn(q, k, v, cfg.n, cfg.scale, out=out))
     t_m = timeit(lambda: hd.mix_attn(q, k, v, cfg.n, cfg.scale, out=out))
     fl_hd = 3 * attn_flops(1, cfg.n, cfg.L, cfg.Hq, cfg.D, "within") + \
         attn_flops(1, cfg.n, cfg.L, cfg.Hq, cfg.D, "mix")
     fl_base = 4 * attn_flops(1, 1, cfg.L, cfg.Hq, cfg.D, "mix")
-    del layers, base, out, out1
+    del layers, base, out, out1, ws1
     torch.cuda.empty_cache()
     return {
         "workload": "n=8 B=1 L=2048 (nL=16384) Hq=32 Hkv=8 D=128; 3 within + 1 mixing layer "
                     "vs n=1 stack of 4 causal layers at L=2048",
         "ms_stack": round(t_hd, 4), "ms_stack_n1": round(t_base, 4),
         "time_ratio_vs_n1": round(t_hd / t_base, 3), "flop_ratio_vs_n1": round(fl_hd / fl_base, 3),
+        "ms_stack_n1_key_split": round(t_base_split, 4),
+        "time_ratio_vs_n1_key_split": round(t_hd / t_base_split, 3),
         "ms_within": round(t_w, 4), "ms_mix": round(t_m, 4),
         "mix_over_within_time": round(t_m / t_w, 3),
         "mix_over_within_flops": round(attn_flops(1, cfg.n, cfg.L, cfg.Hq, cfg.D, "mix") /

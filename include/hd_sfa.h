@@ -52,7 +52,7 @@ typedef enum hd_status {
                                 library's 32-bit index range                     */
     HD_ERR_CAPACITY = 4,     /* KV cache too small for the appended entries      */
     HD_ERR_LAUNCH = 5,       /* the HIP runtime refused a launch                 */
-    HD_ERR_WORKSPACE = 6,    /* decode workspace NULL or smaller than required   */
+    HD_ERR_WORKSPACE = 6,    /* workspace NULL, smaller than required or misaligned */
     HD_ERR_SCRATCH = 7       /* the call needs more than the library's static
                                 scratch (sfa_decode_step_noalloc) holds          */
 } hd_status;
@@ -197,6 +197,45 @@ hd_status sfa_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        uint16_t* out, float* lse, int64_t B, int32_t n, int64_t L,
                        int32_t Hq, int32_t Hkv, int32_t D, float softmax_scale,
                        int32_t mode, hipStream_t stream);
+
+/*
+ * sfa_attn_split_workspace_size -- bytes of device workspace sfa_attn_split
+ * needs for these sizes (0 if no work item of the layer has two key tiles,
+ * or for arguments sfa_attn_split would reject).
+ */
+size_t sfa_attn_split_workspace_size(int64_t B, int32_t n, int64_t L, int32_t Hq,
+                                     int32_t Hkv, int32_t D, int32_t mode);
+
+/*
+ * sfa_attn_split -- sfa_attn_fwd for launches too small to fill the GPU.
+ * The attention is causal, so the work items of a layer (64-query tiles x
+ * packed query heads) end at different key tiles; when there are no more
+ * items than compute units (a base model at n = 1 and batch 1, say), the
+ * longest item sets the time.  Here each item with two or more key tiles is
+ * taken as two units, its first and its second half of the key tiles, by
+ * different workgroups; each unit writes its partial softmax state (running
+ * max m, sum l, unnormalised O) to the workspace and the second one to finish
+ * merges the two (l and O rescaled to the larger m) and writes the output
+ * and lse.  It is the usual split of a softmax over key blocks; the
+ * operation is the one sfa_attn_fwd defines (review, section Method: the two
+ * visibility rules).  With more items than compute units the call is
+ * sfa_attn_fwd itself and the workspace is not touched.
+ *
+ *   workspace  device memory of at least sfa_attn_split_workspace_size()
+ *              bytes, 16-byte aligned, owned by the caller, zero-filled
+ *              before its first use; every call leaves its counters at zero
+ *              again (HD_ERR_WORKSPACE if NULL, short or misaligned when the
+ *              split is taken)
+ * Results: within the forward's tolerance of sfa_attn_fwd, not bitwise (the
+ * merge adds the two halves' sums in another order); the same bits on every
+ * call, whichever half merges.  Calls that overlap on one workspace race.
+ * Other arguments, layouts and errors as sfa_attn_fwd (lse may be NULL).
+ */
+hd_status sfa_attn_split(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         uint16_t* out, float* lse, int64_t B, int32_t n, int64_t L,
+                         int32_t Hq, int32_t Hkv, int32_t D, float softmax_scale,
+                         int32_t mode, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
 
 /*
  * sfa_attn_bwd_workspace_size -- bytes of device workspace sfa_attn_bwd needs

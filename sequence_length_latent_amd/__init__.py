@@ -16,7 +16,8 @@ import torch
 from ._lib import HDError, check, load  # noqa: F401
 
 __all__ = ["expand", "final_stream_rows", "cyclic_replicate", "stream_attn", "mix_attn",
-           "mix_attn_window", "attn_fwd", "attn_bwd", "decode_workspace_size", "decode_step",
+           "mix_attn_window", "attn_fwd", "split_workspace", "attn_split", "attn_bwd",
+           "decode_workspace_size", "decode_step",
            "decode_step_noalloc", "decode_step_paged",
            "HDError", "load", "WITHIN", "MIX"]
 
@@ -161,6 +162,51 @@ def attn_fwd(q, k, v, n: int, scale: float, mode: int, out=None, lse=None, windo
     else:
         out = _attn("sfa_attn_fwd", q, k, v, n, scale, out, lse=lse, mode=mode)
     return out, lse
+
+
+def split_workspace(q, k, n: int, mode: int):
+    """A zero-filled workspace for attn_split with these shapes (uint8 tensor;
+    empty when no split is possible).  Reuse it across calls: every call
+    leaves it ready for the next one."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    B, N, Hq, D = q.shape
+    if n < 1 or N % n:
+        raise ValueError(f"sequence length {N} is not a multiple of n={n}")
+    size = load().sfa_attn_split_workspace_size(B, n, N // n, Hq, k.shape[2], D, int(mode))
+    return torch.zeros(max(int(size), 1), dtype=torch.uint8, device=q.device)
+
+
+def attn_split(q, k, v, n: int, scale: float, mode: int, workspace, out=None, lse=None):
+    """Prefill layer (mode WITHIN or MIX) for launches with no more work items
+    than compute units: each item's key tiles are taken in two halves by
+    different workgroups and merged (sfa_attn_split).  ``workspace`` from
+    split_workspace(); ``lse`` optional [B, Hq, n*L] fp32.  Returns out."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, torch.bfloat16, 4)
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if n < 1 or N % n:
+        raise ValueError(f"sequence length {N} is not a multiple of n={n}")
+    if tuple(k.shape) != (B, N, Hkv, D) or tuple(v.shape) != (B, N, Hkv, D):
+        raise ValueError("k and v must be [B, n*L, Hkv, D] matching q")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, 4)
+    if out.shape != q.shape:
+        raise ValueError("out must match q")
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 3)
+        if tuple(lse.shape) != (B, Hq, N):
+            raise ValueError("lse must be [B, Hq, n*L]")
+    if workspace is None or workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace: a contiguous device tensor from split_workspace()")
+    st = load().sfa_attn_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                               None if lse is None else lse.data_ptr(), B, n, N // n, Hq, Hkv,
+                               D, float(scale), int(mode), workspace.data_ptr(),
+                               workspace.numel() * workspace.element_size(), _stream())
+    check("sfa_attn_split", st)
+    return out
 
 
 def attn_bwd(q, k, v, dout, lse, n: int, scale: float, mode: int, dq=None, dk=None,

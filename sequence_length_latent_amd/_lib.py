@@ -30,6 +30,9 @@ SIGNATURES = {
                                _f32, _i32, _vp]),
     "sfa_attn_fwd_window": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i64, _i32, _i32,
                                       _i32, _f32, _i64, _vp]),
+    "sfa_attn_split_workspace_size": (_sz, [_i64, _i32, _i64, _i32, _i32, _i32, _i32]),
+    "sfa_attn_split": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i64, _i32, _i32, _i32,
+                                 _f32, _i32, _vp, _sz, _vp]),
     "sfa_attn_bwd_workspace_size": (_sz, [_i64, _i32, _i64, _i32]),
     "sfa_attn_bwd": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i64,
                                _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),

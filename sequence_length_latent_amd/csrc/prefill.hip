@@ -54,6 +54,7 @@
 #include "common.h"
 #include "prefill_asm.h"
 
+#include <algorithm>
 #include <cstdlib>
 #include <type_traits>
 
@@ -91,6 +92,12 @@ struct PrefillArgs {
     float c;             // softmax scale * log2(e)
     float* lse;          // optional [B, Hq, N] natural log-sum-exp of each row (training)
     uint32_t Hq, N;
+    // key-split launches (SPLIT kernels only): units n_items + n_split, see
+    // make_item; per (item, wave) a counter and two partial-state slots
+    uint32_t n_units;
+    uint32_t n_split;    // items with two or more key tiles (a prefix of the item order)
+    uint32_t* cnt;       // [n_split * NW], zero between calls
+    float* part;         // [n_split, 2, NW, slot floats]
 };
 
 // Scale modes: the exponent argument of a score s is s * c - m with
@@ -103,10 +110,20 @@ struct PrefillArgs {
 // The softmax issue time of a wave is close to proportional to its
 // instruction bytes, so the shorter form matters.
 constexpr int kScaleAny = 0, kScaleUnit = 1, kScaleLog2 = 2;
+// Floats of one wave's partial softmax state in a key-split launch: per lane
+// its O^T accumulators (D/32 blocks of 16) and (m, l).
+template <int D>
+constexpr int split_slot_floats() { return kWave * (D / 2 + 2); }
+
 // WIN: sliding window (a.window < len); otherwise plain causal.
-template <int D, int MODE, bool WIN>
+// SPLIT: key-split launch (no window): an item with two or more key tiles is
+// taken as two units, its first and second half of the tiles, by different
+// workgroups; each writes its partial softmax state (m, l, O) and the second
+// to finish merges both and writes the output.
+template <int D, int MODE, bool WIN, bool SPLIT>
 __global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 sfa_prefill_kernel(const PrefillArgs a) {
+    static_assert(!(WIN && SPLIT), "a windowed layer is not key-split");
     constexpr int ROWB = D * 2;                // bytes per K/V row
     constexpr int TILE_B = BN * ROWB;          // one K (or V) tile
     constexpr int LOADS = TILE_B / (THREADS * 16);   // 16-byte direct loads per thread per tile
@@ -144,15 +161,16 @@ sfa_prefill_kernel(const PrefillArgs a) {
     // tile counts and the lane's query row); the Q and O row addresses are
     // recomputed from the item index where they are used.
     struct Item {
-        uint32_t id;
+        uint32_t id;          // the item (a key-split unit's item)
         const char* kview;
         const char* vview;
-        int n_kt;             // key tiles up to the item's last (absolute end)
+        int n_kt;             // end of the unit's key tiles (absolute; the item's end unless split)
         int wave_kt;          // key tiles this wave needs (absolute end)
-        int m_lo;             // first key tile of the item (0 without a window)
+        int m_lo;             // first key tile of the unit (0 without a window or split)
         int wave_lo;          // this wave's first key tile
         int lo_end;           // last tile holding a key below some row's window (-1: none)
         uint32_t qi;          // this lane's query row in the view
+        int part;             // key-split: -1 whole item, else 0 / 1 (first / second half)
     };
     // (batch, view, query head) offset of an item, in elements, and its first row
     auto item_head = [&](uint32_t id, uint32_t& q0) -> uint64_t {
@@ -167,8 +185,11 @@ sfa_prefill_kernel(const PrefillArgs a) {
         q0 = qtile * BT + (wave / a.P) * MQ;
         return b * a.q_batch + grp * a.q_group + (uint64_t)(kvh * a.G + hp * a.P + (wave % a.P)) * D;
     };
-    auto make_item = [&](uint32_t id) -> Item {
+    auto make_item = [&](uint32_t unit) -> Item {
         Item it;
+        // key-split units: n_items first halves (whole items when they have
+        // one tile), then the second halves of the first n_split items
+        const uint32_t id = (SPLIT && unit >= a.n_items) ? unit - a.n_items : unit;
         it.id = id;
         const uint32_t qtile = a.n_qtiles - 1 - id / per_tile;
         uint32_t r = id % per_tile;
@@ -185,6 +206,7 @@ sfa_prefill_kernel(const PrefillArgs a) {
         const uint32_t wave_end = min(a.len, q0 + MQ);       // exclusive
         it.wave_kt = q0 < a.len ? (int)((wave_end + BN - 1) / BN) : 0;
         it.qi = q0 + l32;
+        it.part = -1;
         if constexpr (WIN) {
             // oldest visible key of row r: r - W + 1 (clamped at 0)
             const uint32_t f0 = qtile * BT;
@@ -195,16 +217,32 @@ sfa_prefill_kernel(const PrefillArgs a) {
             it.m_lo = 0;
             it.wave_lo = 0;
             it.lo_end = -1;
+            if constexpr (SPLIT) {
+                if (it.n_kt >= 2) {
+                    const int half = (it.n_kt + 1) / 2;
+                    if (unit < a.n_items) {
+                        it.part = 0;
+                        it.n_kt = half;
+                    } else {
+                        it.part = 1;
+                        it.m_lo = half;
+                    }
+                }
+            }
         }
         return it;
     };
-    // window bounds; compile-time zero without a window
-    auto lo_of = [&](const Item& it) -> int { if constexpr (WIN) return it.m_lo; else return 0; };
-    auto wlo_of = [&](const Item& it) -> int { if constexpr (WIN) return it.wave_lo; else return 0; };
+    // first tiles (window or key split); compile-time zero otherwise
+    auto lo_of = [&](const Item& it) -> int { if constexpr (WIN || SPLIT) return it.m_lo; else return 0; };
+    auto wlo_of = [&](const Item& it) -> int {
+        if constexpr (WIN) return it.wave_lo;
+        else if constexpr (SPLIT) return it.m_lo;    // every wave starts at the unit's first tile
+        else return 0;
+    };
     // item taken in round r (snake order over the grid)
     auto item_at = [&](uint32_t r) -> uint32_t {
         const uint32_t g = gridDim.x;
-        return r * g + ((r & 1u) ? (g - 1u - blockIdx.x) : blockIdx.x);
+        return r * g + ((r & 1u) ? (g - 1u - blockIdx.x) : blockIdx.x);   // a unit in key-split launches
     };
 
     // ---- direct global->LDS tile loads ----
@@ -312,6 +350,74 @@ sfa_prefill_kernel(const PrefillArgs a) {
                     *reinterpret_cast<u32x2*>(orow + d) = w;
                 }
         }
+    };
+
+    // ---- key-split units ----
+    // A unit's wave writes its partial state (its O^T accumulators, m and l,
+    // which are in log2 units relative to m) to its slot, then counts itself
+    // in the (item, wave) counter.  The wave that counts second has both
+    // states: it merges them into its registers, writes the output and
+    // clears the counter for the next call; the other one is done.  Neither
+    // waits for the other.  The slots are written and read with device-scope
+    // accesses (they bypass the compute unit's and its XCD's caches where
+    // those are not coherent across the device), and the writes have
+    // completed before the count is taken, so the wave that counts second
+    // reads the other state whole; no cache-wide write-back or invalidation
+    // is needed.  The merge takes both products explicitly (no contraction),
+    // so it gives the same bits whichever half merges.
+    auto merge_split = [&](const Item& it) -> bool {
+        constexpr int SF = split_slot_floats<D>();
+        constexpr int OFL = DBLK * 16 * kWave;     // floats of the accumulators in a slot
+        const uint32_t w = __builtin_amdgcn_readfirstlane(wave);
+        float* const slots = a.part + (size_t)it.id * 2 * NW * SF;
+        uint64_t* const own = reinterpret_cast<uint64_t*>(slots + (size_t)(it.part * NW + w) * SF);
+        uint64_t* const oth = reinterpret_cast<uint64_t*>(slots + (size_t)((it.part ^ 1) * NW + w) * SF);
+        auto pack2 = [](float lo, float hi) -> uint64_t {
+            return (uint64_t)__builtin_bit_cast(uint32_t, lo) | ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
+        };
+        auto lo_of2 = [](uint64_t x) { return __builtin_bit_cast(float, (uint32_t)x); };
+        auto hi_of2 = [](uint64_t x) { return __builtin_bit_cast(float, (uint32_t)(x >> 32)); };
+        // pair k of accumulator block db at (db * 8 + k) * 64 + lane (8-byte units)
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+            for (int k2 = 0; k2 < 8; ++k2)
+                __hip_atomic_store(own + (db * 8 + k2) * kWave + lane,
+                                   pack2(oacc[db][2 * k2], oacc[db][2 * k2 + 1]),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(own + OFL / 2 + lane, pack2(m_run, l_run), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the state is written before it counts
+        uint32_t old = 0;
+        if (lane == 0)
+            old = __hip_atomic_fetch_add(a.cnt + (size_t)it.id * NW + w, 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+        old = __builtin_amdgcn_readfirstlane(old);
+        if (old == 0) return false;
+        const uint64_t ml = __hip_atomic_load(oth + OFL / 2 + lane, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+        {
+#pragma clang fp contract(off)
+            const float mo = lo_of2(ml);
+            const float mn = fmaxf(m_run, mo);
+            const float sw = fast_exp2(m_run - mn), so = fast_exp2(mo - mn);
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db) {
+#pragma unroll
+                for (int k2 = 0; k2 < 8; ++k2) {
+                    const uint64_t x = __hip_atomic_load(oth + (db * 8 + k2) * kWave + lane,
+                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    oacc[db][2 * k2] = oacc[db][2 * k2] * sw + lo_of2(x) * so;
+                    oacc[db][2 * k2 + 1] = oacc[db][2 * k2 + 1] * sw + hi_of2(x) * so;
+                }
+            }
+            l_run = l_run * sw + hi_of2(ml) * so;
+            m_run = mn;
+        }
+        if (lane == 0)
+            __hip_atomic_store(a.cnt + (size_t)it.id * NW + w, 0u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        return true;
     };
 
     // ---- per-lane LDS read offsets (independent of the tile) ----
@@ -486,7 +592,7 @@ sfa_prefill_kernel(const PrefillArgs a) {
             uint32_t id2;
             asm volatile("s_mov_b32 %0, %1" : "=s"(id2) : "s"(nid));
             const Item nx = make_item(id2);
-            issue_q(id2);
+            issue_q(nx.id);                    // the unit's item
             issue(nx.kview, lo_of(nx), kbuf(0));
             if (lo_of(nx) + 1 < nx.n_kt) issue(nx.kview, lo_of(nx) + 1, kbuf(1));
             if (r & 1) issue(nx.vview, lo_of(nx), vbuf(0));
@@ -510,7 +616,7 @@ sfa_prefill_kernel(const PrefillArgs a) {
         // a wave computes P(m) for wave_lo <= m <= last and S(m+1) when m+1 is
         // in that range too (without a window wave_lo = 0)
         const bool do_pv = m >= wlo_of(cur) && m <= last;
-        const bool do_qk = m + 1 >= wlo_of(cur) && m < last;
+        const bool do_qk = m + 1 >= wlo_of(cur) && m < last && (!SPLIT || m + 1 < cur.n_kt);
         if (do_pv && do_qk) {
             if constexpr (D == 128) {
                 if constexpr (PAR == 0) asm volatile(HD_ASM_FULL_D128_P0 : HD_ASM_OUTS_FULL_D128 : HD_ASM_INS_FULL_D128 : HD_ASM_CLOBBERS);
@@ -548,15 +654,15 @@ sfa_prefill_kernel(const PrefillArgs a) {
     // ---- persistent loop over this workgroup's work items ----
     uint32_t round = 0;
     const uint32_t first = item_at(0);
-    if (first >= a.n_items) return;            // uniform over the workgroup
+    if (first >= a.n_units) return;            // uniform over the workgroup
     Item cur = make_item(first);
-    issue_q(first);
+    issue_q(cur.id);
     issue(cur.kview, lo_of(cur), kbuf(0));
     issue(cur.vview, lo_of(cur), vbuf(0));
     if (lo_of(cur) + 1 < cur.n_kt) issue(cur.kview, lo_of(cur) + 1, kbuf(1));
     for (;;) {
         const uint32_t nid = item_at(round + 1);
-        const bool more = nid < a.n_items;
+        const bool more = nid < a.n_units;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
@@ -567,7 +673,7 @@ sfa_prefill_kernel(const PrefillArgs a) {
         for (int i = 0; i < DBLK; ++i) oacc[i] = f32x16{};
         m_run = -INFINITY;
         l_run = 0.f;
-        if (cur.wave_kt > 0) {
+        if (cur.wave_kt > lo_of(cur)) {
             // S of the item's first tile (K slot 0: the score product of parity 1)
             f32x16(&S)[BN / 32] = sc;
             const bf16x8(&Q)[DSTEPS] = qf;
@@ -587,8 +693,12 @@ sfa_prefill_kernel(const PrefillArgs a) {
             const Item nx = make_item(nid);
             issue(nx.vview, lo_of(nx), vbuf(0));
         }
-        store_out(cur.id, cur.qi);
-        if (a.lse != nullptr && hh == 0 && cur.qi < a.len) {
+        bool write_out = true;
+        if constexpr (SPLIT) {
+            if (cur.part >= 0) write_out = merge_split(cur);
+        }
+        if (write_out) store_out(cur.id, cur.qi);
+        if (write_out && a.lse != nullptr && hh == 0 && cur.qi < a.len) {
             // log-sum-exp of the scaled scores: m and l are in log2 units of c * s
             uint32_t r = cur.id % per_tile;
             const uint32_t hp = r % a.n_hpacks;
@@ -635,10 +745,46 @@ uint64_t persistent_workgroups() {
     return g;
 }
 
+// Work items of a layer (see the kernel) and how many have two or more key
+// tiles: the items a key-split launch takes in two halves.
+struct ItemPlan {
+    uint32_t n_qtiles = 0, per_tile = 0, BT = 0, P = 0;
+    uint64_t items = 0, split_items = 0;
+};
+ItemPlan plan_items(int64_t B, int32_t n, int64_t L, int32_t Hq, int32_t Hkv, bool within) {
+    ItemPlan p;
+    const uint64_t len = within ? (uint64_t)L : (uint64_t)n * (uint64_t)L;
+    const uint32_t G = (uint32_t)(Hq / Hkv);
+    p.P = (G % 8 == 0) ? 8u : (G % 4 == 0) ? 4u : ((G % 2 == 0) ? 2u : 1u);
+    p.BT = MQ * (NW / p.P);
+    p.n_qtiles = (uint32_t)((len + p.BT - 1) / p.BT);
+    p.per_tile = (uint32_t)B * (within ? (uint32_t)n : 1u) * (uint32_t)Hkv * (G / p.P);
+    p.items = (uint64_t)p.n_qtiles * p.per_tile;
+    // items are listed longest first; those of query tile qt end at key tile
+    // ceil(min(len, (qt + 1) * BT) / BN)
+    uint64_t qsplit = 0;
+    for (uint64_t qt = 0; qt < p.n_qtiles; ++qt)
+        if (std::min<uint64_t>(len, (qt + 1) * p.BT) > (uint64_t)BN) ++qsplit;
+    p.split_items = qsplit * p.per_tile;
+    return p;
+}
+
+// Workspace of a key-split launch: the (item, wave) counters, then two
+// partial-state slots per (item, wave).
+size_t split_counter_bytes(uint64_t split_items) {
+    return ((size_t)split_items * NW * sizeof(uint32_t) + 255) & ~(size_t)255;
+}
+size_t split_workspace_bytes(uint64_t split_items, int32_t D) {
+    if (split_items == 0) return 0;
+    const size_t slot = (size_t)(D == 128 ? split_slot_floats<128>() : split_slot_floats<64>()) * sizeof(float);
+    return split_counter_bytes(split_items) + (size_t)split_items * 2 * NW * slot;
+}
+
 hd_status launch_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          uint16_t* out, int64_t B, int32_t n, int64_t L, int32_t Hq,
                          int32_t Hkv, int32_t D, float scale, hipStream_t stream,
-                         bool within, int64_t window, float* lse = nullptr) {
+                         bool within, int64_t window, float* lse = nullptr,
+                         void* split_ws = nullptr, size_t split_ws_bytes = 0) {
     // window: 0 = none (plain causal), else >= 1 rows of the view
     if (B < 0 || L < 0 || n < 1 || Hq < 1 || Hkv < 1 || window < 0) return HD_ERR_SHAPE;
     if (!scale_ok(scale)) return HD_ERR_SHAPE;
@@ -680,24 +826,40 @@ hd_status launch_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v
     if (items > 0x7fffffffULL) return HD_ERR_UNSUPPORTED;
     a.n_items = (uint32_t)items;
     const uint64_t wgs = persistent_workgroups();
-    const uint64_t blocks = items < wgs ? items : wgs;
     // a window at least as long as the view masks nothing: the causal kernel
     const bool win = window > 0 && window < (int64_t)a.len;
     a.window = win ? (uint32_t)window : 0u;
+    // key split: with a workspace, for a launch that gives no compute unit
+    // more than one item (the causal items then differ in length up to the
+    // number of key tiles and the longest sets the time)
+    const ItemPlan plan = plan_items(B, n, L, Hq, Hkv, within);
+    const bool split = split_ws != nullptr && !win && items <= wgs && plan.split_items > 0;
+    a.n_split = split ? (uint32_t)plan.split_items : 0u;
+    a.n_units = (uint32_t)items + a.n_split;
+    a.cnt = nullptr;
+    a.part = nullptr;
+    if (split) {
+        if (split_ws_bytes < split_workspace_bytes(plan.split_items, D) || !aligned16(split_ws))
+            return HD_ERR_WORKSPACE;
+        a.cnt = static_cast<uint32_t*>(split_ws);
+        a.part = reinterpret_cast<float*>(static_cast<char*>(split_ws) + split_counter_bytes(plan.split_items));
+    }
+    const uint64_t blocks = a.n_units < wgs ? a.n_units : wgs;
     const int mode = a.c == 1.f ? kScaleLog2 : (scale == 1.f ? kScaleUnit : kScaleAny);
-    auto pick = [&](auto d, auto w) {
+    auto pick = [&](auto d, auto w, auto sp) {
         constexpr int DD = decltype(d)::value;
         constexpr bool WW = decltype(w)::value;
-        return mode == kScaleLog2 ? sfa_prefill_kernel<DD, kScaleLog2, WW>
-             : mode == kScaleUnit ? sfa_prefill_kernel<DD, kScaleUnit, WW>
-                                  : sfa_prefill_kernel<DD, kScaleAny, WW>;
+        constexpr bool SS = decltype(sp)::value;
+        return mode == kScaleLog2 ? sfa_prefill_kernel<DD, kScaleLog2, WW, SS>
+             : mode == kScaleUnit ? sfa_prefill_kernel<DD, kScaleUnit, WW, SS>
+                                  : sfa_prefill_kernel<DD, kScaleAny, WW, SS>;
     };
     using D128 = std::integral_constant<int, 128>;
     using D64 = std::integral_constant<int, 64>;
-    using W1 = std::true_type;
-    using W0 = std::false_type;
-    auto kern = D == 128 ? (win ? pick(D128{}, W1{}) : pick(D128{}, W0{}))
-                         : (win ? pick(D64{}, W1{}) : pick(D64{}, W0{}));
+    using T1 = std::true_type;
+    using T0 = std::false_type;
+    auto kern = D == 128 ? (win ? pick(D128{}, T1{}, T0{}) : split ? pick(D128{}, T0{}, T1{}) : pick(D128{}, T0{}, T0{}))
+                         : (win ? pick(D64{}, T1{}, T0{}) : split ? pick(D64{}, T0{}, T1{}) : pick(D64{}, T0{}, T0{}));
     kern<<<dim3((uint32_t)blocks), dim3(THREADS), 0, stream>>>(a);
     return launch_status();
 }
@@ -731,6 +893,28 @@ extern "C" hd_status sfa_attn_fwd(const uint16_t* q, const uint16_t* k, const ui
     if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return HD_ERR_SHAPE;
     return hdsfa::launch_prefill(q, k, v, out, B, n, L, Hq, Hkv, D, softmax_scale, stream,
                                  /*within=*/mode == 0, /*window=*/0, lse);
+}
+
+extern "C" size_t sfa_attn_split_workspace_size(int64_t B, int32_t n, int64_t L, int32_t Hq,
+                                                int32_t Hkv, int32_t D, int32_t mode) {
+    if (B < 1 || n < 1 || L < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return 0;
+    if ((D != 64 && D != 128) || (mode != 0 && mode != 1)) return 0;
+    const hdsfa::ItemPlan p = hdsfa::plan_items(B, n, L, Hq, Hkv, mode == 0);
+    return hdsfa::split_workspace_bytes(p.split_items, D);
+}
+
+extern "C" hd_status sfa_attn_split(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                    uint16_t* out, float* lse, int64_t B, int32_t n, int64_t L,
+                                    int32_t Hq, int32_t Hkv, int32_t D, float softmax_scale,
+                                    int32_t mode, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+    if (mode != 0 && mode != 1) return HD_ERR_SHAPE;
+    if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return HD_ERR_SHAPE;
+    if (workspace == nullptr && sfa_attn_split_workspace_size(B, n, L, Hq, Hkv, D, mode) > 0)
+        return HD_ERR_WORKSPACE;
+    return hdsfa::launch_prefill(q, k, v, out, B, n, L, Hq, Hkv, D, softmax_scale, stream,
+                                 /*within=*/mode == 0, /*window=*/0, lse, workspace,
+                                 workspace_bytes);
 }
 
 extern "C" hd_status sfa_mix_attn_window(const uint16_t* q, const uint16_t* k,

@@ -36,7 +36,8 @@ def test_every_declared_symbol_is_exported(lib):
                           "sfa_attn_fwd_window", "sfa_attn_bwd_window",
                           "sfa_decode_workspace_size", "sfa_decode_step",
                           "sfa_decode_step_window", "sfa_decode_step_paged",
-                          "sfa_decode_step_noalloc"}
+                          "sfa_decode_step_noalloc", "sfa_attn_split_workspace_size",
+                          "sfa_attn_split"}
     for name in names:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, name
@@ -306,3 +307,45 @@ def test_softmax_scale_must_be_finite_and_positive(lib):
                                           FAKE, 1 << 30, FAKE, None, None) == SHAPE
         assert lib.sfa_decode_step_paged(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 8, 2, 128, 16, 64, 8,
                                          10, 1, 0, sc, FAKE, 1 << 30, FAKE, None, None) == SHAPE
+
+
+def _split_bytes(items_split, D):
+    """Workspace of the key-split forward, restated: a 4-byte counter per
+    (item, wave) rounded up to 256 bytes, then two slots per (item, wave) of
+    64 lanes x (D/2 accumulators + m + l) floats."""
+    counters = -(-items_split * 8 * 4 // 256) * 256
+    return counters + items_split * 2 * 8 * 64 * (D // 2 + 2) * 4
+
+
+def test_split_workspace_size(lib):
+    f = lib.sfa_attn_split_workspace_size
+    # n = 1, L = 2048, 32 / 8 heads: 32 query tiles of 64 rows x 8 KV heads;
+    # all but the first query tile have two or more key tiles
+    assert f(1, 1, 2048, 32, 8, 128, 1) == _split_bytes(31 * 8, 128)
+    # within-stream, n = 4, L = 1024, batch 2: 16 query tiles x 2 x 4 x 8 views
+    assert f(2, 4, 1024, 32, 8, 128, 0) == _split_bytes(15 * 2 * 4 * 8, 128)
+    # G = 8 packs 32 query rows per item: tiles 0 and 1 end inside key tile 0
+    assert f(1, 1, 256, 16, 2, 64, 1) == _split_bytes(6 * 2, 64)
+    # G = 2 packs 128 rows per item: every item has two or more key tiles
+    assert f(1, 2, 200, 4, 2, 128, 1) == _split_bytes(4 * 2, 128)
+    assert f(1, 1, 64, 8, 2, 128, 1) == 0          # one key tile: nothing to split
+    for bad in ((0, 1, 64, 8, 2, 128, 1), (1, 1, 64, 8, 3, 128, 1), (1, 1, 64, 8, 2, 96, 1),
+                (1, 1, 64, 8, 2, 128, 2), (1, 0, 64, 8, 2, 128, 1)):
+        assert f(*bad) == 0, bad
+
+
+def test_split_validation(lib):
+    f = lib.sfa_attn_split
+    need = lib.sfa_attn_split_workspace_size(1, 1, 2048, 32, 8, 128, 1)
+    args = (1, 1, 2048, 32, 8, 128, 1.0)
+    assert f(FAKE, FAKE, FAKE, FAKE, None, *args, 2, FAKE, need, None) == SHAPE      # mode
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE + 2, *args, 1, FAKE, need, None) == SHAPE  # lse align
+    assert f(FAKE, FAKE, FAKE, FAKE, None, *args, 1, None, need, None) == WS         # no workspace
+    assert f(None, FAKE, FAKE, FAKE, None, *args, 1, FAKE, need, None) == NULL
+    # 256 items: split on a GPU of 256 compute units (the count taken when
+    # none can be queried): a short or misaligned workspace is refused
+    assert f(FAKE, FAKE, FAKE, FAKE, None, *args, 1, FAKE, need - 1, None) == WS
+    assert f(FAKE, FAKE, FAKE, FAKE, None, *args, 1, FAKE + 8, need, None) == WS
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 1, 1, 2048, 32, 8, 96, 1.0, 1, FAKE, need, None) == UNSUP
+    # a one-tile layer needs no workspace: the check passes it on (zero work: OK)
+    assert f(None, None, None, None, None, 0, 1, 64, 8, 2, 128, 1.0, 1, None, 0, None) == OK
