@@ -433,11 +433,50 @@ dkv_kernel(const BwdArgs a) {
                 qa[e] = lds16(qt + qb * MQ * ROWB + doff[e]);
                 oa[e] = lds16(ot + qb * MQ * ROWB + doff[e]);
             }
-            f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-            for (int e = 0; e < DSTEPS; ++e) {
-                s = mfma(qa[e], kf[e], s);
-                dp = mfma(oa[e], vf[e], dp);
+            // the score products in one block: the wave's K / V fragments stay in
+            // the accumulation registers (they are read only here), which leaves
+            // the vector registers to S and dP (no moves out of accumulation
+            // registers before the softmax).  Entry pad: VALU -> MFMA operand
+            // reads; exit pad: MFMA -> VALU result reads.
+            f32x16 s, dp;
+            if constexpr (DSTEPS == 8) {
+                asm volatile("s_nop 4\n\t"
+                         "v_mfma_f32_32x32x16_bf16 %[s], %[q0], %[k0], 0\n\t"
+                         "v_mfma_f32_32x32x16_bf16 %[d], %[o0], %[v0], 0\n\t"
+                         "v_mfma_f32_32x32x16_bf16 %[s], %[q1], %[k1], %[s]\n\t"
+                         "v_mfma_f32_32x32x16_bf16 %[d], %[o1], %[v1], %[d]\n\t"
+                         "v_mfma_f32_32x32x16_bf16 %[s], %[q2], %[k2], %[s]\n\t"
+                         "v_mfma_f32_32x32x16_bf16 %[d], %[o2], %[v2], %[d]\n\t"
+                         "v_mfma_f32_32x32x16_bf16 %[s], %[q3], %[k3], %[s]\n\t"
+                         "v_mfma_f32_32x32x16_bf16 %[d], %[o3], %[v3], %[d]\n\t"
+                         "v_mfma_f32_32x32x16_bf16 %[s], %[q4], %[k4], %[s]\n\t"
+                         "v_mfma_f32_32x32x16_bf16 %[d], %[o4], %[v4], %[d]\n\t"
+                         "v_mfma_f32_32x32x16_bf16 %[s], %[q5], %[k5], %[s]\n\t"
+                         "v_mfma_f32_32x32x16_bf16 %[d], %[o5], %[v5], %[d]\n\t"
+                         "v_mfma_f32_32x32x16_bf16 %[s], %[q6], %[k6], %[s]\n\t"
+                         "v_mfma_f32_32x32x16_bf16 %[d], %[o6], %[v6], %[d]\n\t"
+                         "v_mfma_f32_32x32x16_bf16 %[s], %[q7], %[k7], %[s]\n\t"
+                         "v_mfma_f32_32x32x16_bf16 %[d], %[o7], %[v7], %[d]\n\t"
+                         "s_nop 7\n\t"
+                         "s_nop 7\n\t"
+                         "s_nop 7\n\t"
+                         : [s] "=&v"(s), [d] "=&v"(dp)
+                         : [q0] "v"(qa[0]), [q1] "v"(qa[1]), [q2] "v"(qa[2]), [q3] "v"(qa[3]), [q4] "v"(qa[4]), [q5] "v"(qa[5]), [q6] "v"(qa[6]), [q7] "v"(qa[7]), [o0] "v"(oa[0]), [o1] "v"(oa[1]), [o2] "v"(oa[2]), [o3] "v"(oa[3]), [o4] "v"(oa[4]), [o5] "v"(oa[5]), [o6] "v"(oa[6]), [o7] "v"(oa[7]), [k0] "a"(kf[0]), [k1] "a"(kf[1]), [k2] "a"(kf[2]), [k3] "a"(kf[3]), [k4] "a"(kf[4]), [k5] "a"(kf[5]), [k6] "a"(kf[6]), [k7] "a"(kf[7]), [v0] "a"(vf[0]), [v1] "a"(vf[1]), [v2] "a"(vf[2]), [v3] "a"(vf[3]), [v4] "a"(vf[4]), [v5] "a"(vf[5]), [v6] "a"(vf[6]), [v7] "a"(vf[7]));
+            } else {
+                asm volatile("s_nop 4\n\t"
+                         "v_mfma_f32_32x32x16_bf16 %[s], %[q0], %[k0], 0\n\t"
+                         "v_mfma_f32_32x32x16_bf16 %[d], %[o0], %[v0], 0\n\t"
+                         "v_mfma_f32_32x32x16_bf16 %[s], %[q1], %[k1], %[s]\n\t"
+                         "v_mfma_f32_32x32x16_bf16 %[d], %[o1], %[v1], %[d]\n\t"
+                         "v_mfma_f32_32x32x16_bf16 %[s], %[q2], %[k2], %[s]\n\t"
+                         "v_mfma_f32_32x32x16_bf16 %[d], %[o2], %[v2], %[d]\n\t"
+                         "v_mfma_f32_32x32x16_bf16 %[s], %[q3], %[k3], %[s]\n\t"
+                         "v_mfma_f32_32x32x16_bf16 %[d], %[o3], %[v3], %[d]\n\t"
+                         "s_nop 7\n\t"
+                         "s_nop 7\n\t"
+                         "s_nop 7\n\t"
+                         : [s] "=&v"(s), [d] "=&v"(dp)
+                         : [q0] "v"(qa[0]), [q1] "v"(qa[1]), [q2] "v"(qa[2]), [q3] "v"(qa[3]), [o0] "v"(oa[0]), [o1] "v"(oa[1]), [o2] "v"(oa[2]), [o3] "v"(oa[3]), [k0] "a"(kf[0]), [k1] "a"(kf[1]), [k2] "a"(kf[2]), [k3] "a"(kf[3]), [v0] "a"(vf[0]), [v1] "a"(vf[1]), [v2] "a"(vf[2]), [v3] "a"(vf[3]));
             }
             // the transposed operands of dV^T and dK^T, read while P and dS form
             bf16x8 ot8[DBLK][2], qt8[DBLK][2];
