@@ -83,10 +83,18 @@ __device__ __forceinline__ bf16x8 lds16(const unsigned char* p) {
     return *reinterpret_cast<const bf16x8*>(p);
 }
 
-// x = hi + lo with both halves in bf16 (lo carries the rounding error of hi)
+// x = hi + lo with both halves in bf16 (lo carries the rounding error of hi).
+// hi is read back as floats from its packed words (element 2k in the low
+// half, 2k + 1 in the high half: a shift and a mask), not converted again.
 __device__ __forceinline__ void split_bf16(const f32x8& x, bf16x8& hi, bf16x8& lo) {
     hi = to_bf16x8(x);
-    const f32x8 h = __builtin_convertvector(hi, f32x8);
+    const u32x4 w = __builtin_bit_cast(u32x4, hi);
+    f32x8 h;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        h[2 * k] = __builtin_bit_cast(float, w[k] << 16);
+        h[2 * k + 1] = __builtin_bit_cast(float, w[k] & 0xffff0000u);
+    }
     lo = to_bf16x8(x - h);
 }
 
@@ -355,6 +363,7 @@ dkv_kernel(const BwdArgs a) {
     const uint32_t per_head = nq - qt_lo;
     const uint32_t n_stage = a.G * per_head;
     const uint32_t q_row_b = (uint32_t)a.q_row * 2u;
+    float lse_next = 0.f;                                // wave 0: the next stage's lse, one row per lane
     auto issue = [&](uint32_t t, unsigned char* buf) {
         const uint32_t h = kvh * a.G + t / per_head;
         const uint32_t r0 = (qt_lo + t % per_head) * BN;
@@ -373,11 +382,12 @@ dkv_kernel(const BwdArgs a) {
                 (void __attribute__((address_space(3)))*)(buf + TILE_B + (wave * LOADS + j) * 1024), 16, 0, 0);
         }
         if (wave == 0) {
-            // lse and delta of the tile's 64 rows (positions row * groups + grp)
+            // lse and delta of the tile's 64 rows (positions row * groups + grp):
+            // delta straight to LDS, lse to a register, which the stage's top
+            // scales to log2 units once per row and writes to LDS
             const uint32_t row = min(r0 + (uint32_t)lane, a.len - 1u);
             const uint64_t s = ((uint64_t)b * a.Hq + h) * a.N + (uint64_t)row * a.groups + grp;
-            __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(a.lse + s),
-                (void __attribute__((address_space(3)))*)(buf + 2 * TILE_B), 4, 0, 0);
+            lse_next = a.lse[s];
             __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(a.delta + s),
                 (void __attribute__((address_space(3)))*)(buf + 2 * TILE_B + BN * 4), 4, 0, 0);
         }
@@ -412,6 +422,8 @@ dkv_kernel(const BwdArgs a) {
     if (n_stage > 0) issue(0, smem);
     for (uint32_t t = 0; t < n_stage; ++t) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (wave == 0)
+            reinterpret_cast<float*>(smem + (t & 1) * STAGE_B + 2 * TILE_B)[lane] = lse_next * kLog2e;
         __syncthreads();
         if (t + 1 < n_stage) issue(t + 1, smem + ((t + 1) & 1) * STAGE_B);
         const unsigned char* st = smem + (t & 1) * STAGE_B;
@@ -508,7 +520,7 @@ dkv_kernel(const BwdArgs a) {
                         for (int j = 0; j < 4; ++j) {
                             const int it = 4 * g4 + j;
                             const int off = 8 * g4 + j;
-                            float p = fast_exp2(__builtin_fmaf(s[it], a.c, -l4[j] * kLog2e));
+                            float p = fast_exp2(__builtin_fmaf(s[it], a.c, -l4[j]));
                             if constexpr (MASKED) {
                                 bool drop = (off + rel < 0) | (rs + (uint32_t)off + 4u * hh >= a.len);
                                 if constexpr (WIN) drop = drop | (off + rel >= (int)a.window);
