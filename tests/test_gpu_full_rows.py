@@ -7,7 +7,8 @@ thirty-two.  The code between items (the next item's Q and first K/V tiles
 requested during the last key tile, the LDS ring slots carried across items,
 the output leaving through a free V slot) runs only there, so these tests
 compare every row of every head (long context: every row of one full
-(batch, KV head) group) with the oracle at those shapes, and check that
+(batch, KV head) group) with the oracle at those shapes (gradients: every KV
+group of the n4 layers and one of the n8 stack's mixing layer), and check that
 running the same call on other grid sizes (1, 7, 100 and 300 workgroups, set
 through HD_SFA_PREFILL_WORKGROUPS) changes no output bit.  The oracle runs
 over (batch, head) units in a thread pool with one BLAS thread each.
@@ -96,6 +97,28 @@ def test_attn_bwd_n4_every_kv_group(mode):
         assert_close(gq[b:b + 1, :, g * G:(g + 1) * G], rq, "dq " + w, c10=False)
         assert_close(gk[b:b + 1, :, g:g + 1], rk, "dk " + w, c10=False)
         assert_close(gv[b:b + 1, :, g:g + 1], rv, "dv " + w, c10=False)
+
+
+# ---------------------------------------------------------------------------
+# gradients of the n8 stack's mixing layer (16384 positions): a key there sums
+# dS over four times as many query rows as in the n4 layer, which is where the
+# bf16 operands' rounding error grows; one full (batch, KV head) group
+# ---------------------------------------------------------------------------
+def test_attn_bwd_n8_mixing_one_kv_group():
+    cfg = si.N8STACK
+    q, k, v = si.prefill_qkv(cfg, device=DEV)
+    do = si.randn_bf16(q.shape, 1.0, 7100, DEV)
+    _, lse = hd.attn_fwd(q, k, v, cfg.n, cfg.scale, MIX)
+    dq, dk, dv = hd.attn_bwd(q, k, v, do, lse, cfg.n, cfg.scale, MIX)
+    torch.cuda.synchronize()
+    G = cfg.Hq // cfg.Hkv
+    g = 3
+    rq, rk, rv, _ = oracle.prefill_backward_ref(*(si.bits(t) for t in (q, k, v, do)), cfg.n, MIX,
+                                                 cfg.scale, heads=[g], batches=[0])
+    w = f"n8 mixing b=0 g={g}"
+    assert_close(f64(dq[:, :, g * G:(g + 1) * G]), rq, "dq " + w, c10=False)
+    assert_close(f64(dk[:, :, g:g + 1]), rk, "dk " + w, c10=False)
+    assert_close(f64(dv[:, :, g:g + 1]), rv, "dv " + w, c10=False)
 
 
 # ---------------------------------------------------------------------------
