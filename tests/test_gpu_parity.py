@@ -308,6 +308,8 @@ BWD_SWEEP = [
     (4, 1, 129, 8, 1, 128, MIX),       # a partial last key tile of 128
     (5, 1, 40, 16, 2, 128, WITHIN),    # P = 8 packing
     (1, 1, 300, 2, 2, 128, MIX),       # P = 1
+    (4, 1, 96, 32, 2, 128, MIX),       # 16 query heads per KV head (the long-context ratio): two packs of 8
+    (2, 1, 100, 6, 2, 64, WITHIN),     # 3 query heads per KV head: three packs of 1
 ]
 
 
