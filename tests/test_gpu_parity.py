@@ -172,6 +172,8 @@ SWEEP = [
     (4, 1, 129, 32, 8, 128),
     (3, 1, 96, 16, 1, 128),
     (8, 1, 33, 2, 2, 64),
+    (2, 1, 65, 6, 2, 128),      # 3 query heads per KV head: packs of 1
+    (3, 1, 50, 12, 2, 64),      # 6 per KV head: packs of 2
 ]
 
 
@@ -685,6 +687,9 @@ def test_decode_other_shapes(mode):
     # n=8, G=8 -> 64 rows in mixing mode (two 32-row blocks)
     cfg = si.DecodeCfg("d8", 10, S=2, n=8, T=70, Hq=8, Hkv=1, D=128, scale=0.09)
     _decode_case(cfg, S=2, T=70, tb=[70, 31], mode=mode)
+    # G=3 (odd): 12 rows in mixing mode, 3 per stream view
+    cfg = si.DecodeCfg("d3g", 19, S=3, n=4, T=150, Hq=6, Hkv=2, D=128, scale=0.1)
+    _decode_case(cfg, S=3, T=150, tb=[150, 64, 1], mode=mode)
 
 
 @pytest.mark.parametrize("mode", [WITHIN, MIX])
