@@ -65,8 +65,9 @@ int hd_abi_version(void);
 
 /*
  * hd_expand -- embedding expansion and interleave.
- * Review, section Method ("n streams with independent embedding tables",
- * "length-nL sequence"); README, section Key Idea, items 1 and 2.
+ * Review, section Method (every token becomes n streams, each stream with an
+ * embedding table of its own, laid out as one sequence of length nL); README,
+ * section Key Idea, items 1 and 2.
  *
  *   out[b, t*n + s, :] = tables[s, ids[b, t], :]   for b < B, t < L, s < n
  *
@@ -120,8 +121,8 @@ hd_status hd_cyclic_replicate(const uint16_t* tables, int32_t n_old, int64_t V, 
 
 /*
  * sfa_stream_attn -- within-stream causal attention over the expanded
- * sequence (prefill).  Review, section Method: most layers attend only within
- * their own stream, at a cost of order n*L^2.
+ * sequence (prefill).  Review, section Method: the majority of layers keep each
+ * stream to itself, at a cost of order n*L^2.
  *
  *   O[b, p(t,s), h] = sum over t' <= t of
  *       softmax_t'( scale * q[b,p(t,s),h] . k[b,p(t',s),g] ) v[b,p(t',s),g]
@@ -162,8 +163,8 @@ hd_status sfa_mix_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 
 /*
  * sfa_mix_attn_window -- mixing attention with the sliding-window pattern
- * (prefill).  Review, section Method: the mixing layers follow the base
- * model's own attention pattern, sliding-window or full (the 80B model has 23
+ * (prefill).  Review, section Method: the mixing layers keep whatever pattern
+ * the base model used, sliding-window or full (the 80B model has 23
  * sliding-window mixing layers of 49).  The pages give no window size; here
  * the window W is counted in positions of the interleaved length-nL order
  * (a base-model window of w tokens is W = n*w):

@@ -9,11 +9,11 @@ Everything here is float64 NumPy computed from the exact bf16 input bits.  Each
 function names the passage it follows:
 
 * "Hidden Decoding at Scale" review (romaanj.github.io), section *Method*: each
-  token becomes n streams through n independent embedding tables and the
-  backbone runs once over the length-nL sequence; most layers attend only inside
-  their own stream (cost of order nL^2), a few layers mix streams with the base
-  model's own (full causal) pattern; the intermediate streams' KV is retained
-  so later tokens read it as context.
+  token becomes n streams, each read from an embedding table of its own, and
+  the backbone runs once over the length-nL sequence; in the majority of layers
+  a position sees only its own stream (cost of order nL^2), and a few layers let
+  streams see each other with the base model's (full causal) pattern; the
+  intermediate streams' KV is retained so later tokens read it as context.
 * arXiv 2607.08186 abstract page: SFA makes the attention cost grow roughly
   linearly in n instead of quadratically.
 * Tencent/Sequential-Hidden-Decoding README, *Key Idea* items 1, 2 and 4.
@@ -29,7 +29,7 @@ Readings where the pages are silent (each listed in the design notes):
   R6 query head h reads KV head h // (Hq / Hkv);
   R7 an out-of-range token id yields an all-zero row and raises a flag;
   R13 a sliding-window mixing layer (review, *Method*: the mixing layers
-     follow the base model's own pattern, sliding-window or full) has a window
+     keep the base model's pattern, sliding-window or full) has a window
      W counted in positions of the interleaved order: position i sees
      i - W < j <= i (the pages give no W; a base window of w tokens is W = n*w).
 
@@ -122,10 +122,10 @@ def cyclic_replicate_ref(tables, n_new):
 def visible(i, j, n, mode, window=None):
     """True where key position j is visible to query position i.
 
-    Within-stream (review, *Method*: "attend only within their own stream"):
+    Within-stream (review, *Method*: a position sees only its own stream):
         j and i hold the same stream (j = i mod n) and j is not later than i
         (reading R3, so a query sees itself).
-    Mixing, full pattern (review, *Method*: the base model's own full causal
+    Mixing, full pattern (review, *Method*: the base model's full causal
         pattern, here over the interleaved order, reading R4): j <= i.
     Mixing, sliding-window pattern (same passage; reading R13): additionally
         j > i - window.

@@ -2,10 +2,11 @@
 // sfa_mix_attn_window, and the training forwards sfa_attn_fwd and
 // sfa_attn_fwd_window, which also write each row's log-sum-exp).
 //
-// "Hidden Decoding at Scale" review, section Method: most layers attend only
-// within their own stream (cost of order n*L^2), a few mix streams with the
-// base model's full causal pattern over the length-nL sequence.  The arXiv
-// 2607.08186 abstract: this keeps attention cost roughly linear in n.
+// "Hidden Decoding at Scale" review, section Method: in the majority of layers a
+// position sees only its own stream (cost of order n*L^2); the few others let
+// streams see each other with the base model's full causal pattern over the
+// length-nL sequence.  The arXiv 2607.08186 abstract: so the attention cost
+// grows about linearly with n rather than with its square.
 //
 // One kernel serves both layer kinds.  It runs causal attention over a
 // strided *view* of the interleaved sequence:

@@ -1,8 +1,8 @@
 """Layer schedules of Stream-Factorized Attention and a multi-layer paged decode.
 
-"Hidden Decoding at Scale" review, section Method: most layers attend only
-within their own stream and a few mix streams with the base model's own
-pattern, sliding-window or full; the 80B model has 6 full + 23 sliding-window
+"Hidden Decoding at Scale" review, section Method: the majority of layers keep
+each stream to itself, and the rest let streams see each other with the base
+model's sliding-window or full pattern; the 80B model has 6 full + 23 sliding-window
 + 20 within-stream layers out of 49, the 617B model 25 full + 69
 within-stream out of 94.  The pages give the counts, not the order: here the
 layers of each kind are spread evenly over the depth (the order changes
