@@ -87,8 +87,8 @@ hd_status hd_expand(const int32_t* ids, int64_t B, int64_t L,
 
 /*
  * hd_final_stream_rows -- the rows the next-token loss reads.  Review, section
- * Method: cross-entropy is applied only at the final stream's positions, the
- * first n-1 streams being latent computation states.
+ * Method: the next-token loss is taken only where each token's last stream
+ * sits; the earlier n-1 streams carry no loss and serve as latent states.
  *
  *   out[b, t, :] = x[b, t*n + n-1, :]   for b < B, t < L
  *
@@ -148,9 +148,9 @@ hd_status sfa_stream_attn(const uint16_t* q, const uint16_t* k, const uint16_t* 
 
 /*
  * sfa_mix_attn -- mixing attention, full causal pattern over the interleaved
- * length-nL order (prefill).  Review, section Method: a few layers mix
- * streams following the base model's own (full) attention pattern, reading
- * the retained intermediate-stream KV.
+ * length-nL order (prefill).  Review, section Method: a few layers let the
+ * streams see each other with the base model's (full) pattern, so they read
+ * the retained KV of the intermediate streams.
  *
  *   O[b, i, h] = sum over j <= i of softmax_j(scale * q[b,i,h] . k[b,j,g]) v[b,j,g]
  *
