@@ -1,7 +1,6 @@
 """C-ABI library checks that need no GPU: it loads, exports every symbol the
 header declares, and rejects invalid arguments on the host before launching
 anything (these paths return before any HIP call)."""
-import ctypes
 import os
 import re
 
