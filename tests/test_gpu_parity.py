@@ -42,7 +42,11 @@ def test_expand_tiny_bit_exact():
 
 
 @pytest.mark.parametrize("n,B,L,V,H", [(1, 1, 1, 7, 8), (3, 2, 33, 50, 24), (8, 1, 100, 300, 64),
-                                       (5, 3, 17, 1000, 4096), (2, 1, 1024, 64, 136)])
+                                       (5, 3, 17, 1000, 4096), (2, 1, 1024, 64, 136),
+                                       # around the one-row-per-workgroup limit of 512 chunks:
+                                       # 256 chunks (two rows per workgroup), 513 (a second pass
+                                       # for one thread), 1024 (two chunks per thread)
+                                       (2, 1, 50, 30, 2048), (1, 2, 9, 11, 4104), (1, 1, 40, 20, 8192)])
 def test_expand_shapes_bit_exact(n, B, L, V, H):
     seed = 1000 + n * 7 + L
     tab = _rand((n, V, H), 0.02, seed, "cpu")
