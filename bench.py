@@ -62,18 +62,31 @@ def decode_bytes(S, n, T, Hkv, D):
     return S * (T + 1) * n * Hkv * D * 2 * 2
 
 
+# the sources that make up each measured kernel (its file, the generated
+# assembly it includes, the shared header), hashed in this order
+KERNEL_SOURCES = {"prefill_source_sha256": ("prefill.hip", "prefill_asm.h", "common.h"),
+                  "decode_source_sha256": ("decode.hip", "common.h")}
+
+
+def kernel_source_sha256(key):
+    """SHA-256 over the bytes of a kernel's source files (KERNEL_SOURCES)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[key]:
+        with open(os.path.join(ROOT, "sequence_length_latent_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
 def measured_traffic(kernel, src):
     """HBM bytes per launch of `kernel` (read + write, averaged over the
     within-stream and mixing launches) from the rocprofv3 FETCH_SIZE /
     WRITE_SIZE summary in profiles/traffic.json -- only if that summary was
     taken on the current kernel source, else None."""
-    import hashlib
     try:
         t = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
-        cur = hashlib.sha256(open(os.path.join(ROOT, "sequence_length_latent_amd", "csrc", src),
-                                  "rb").read()).hexdigest()
         key = "prefill_source_sha256" if src == "prefill.hip" else "decode_source_sha256"
-        if t.get(key) != cur:
+        if t.get(key) != kernel_source_sha256(key):
             return None
         per = t[kernel]
         return round(sum(v["read"] + v["write"] for v in per.values()) / len(per))
